@@ -1,0 +1,255 @@
+"""Plain, slow, obviously correct CPU reference of the packed-attention hot path.
+
+TEST INFRASTRUCTURE ONLY: the product path must never import this module.
+It shares no code with the HIP library or its binding.
+
+What it computes (the hot path of one H3 denoiser block, as described on the
+pages "H3 Runtime Current State" and "H3 Blackwell Runtime Plan"):
+
+1. Q/K RMSNorm per (token, head) over the head dimension
+   ("H3 Runtime Current State", Owned Performance Kernels: the entry kernel
+   fuses Q/K RMSNorm with split-half RoPE; "H3 Blackwell Runtime Plan",
+   2026-08-15 Handoff: fused Q/K RMS + RoPE + HND layout).
+2. 3-axis (t, h, w) split-half RoPE ("H3 Blackwell Runtime Plan",
+   Architecture: 3-axis RoPE; "H3 Runtime Current State", Owned Performance
+   Kernels: split-half RoPE).
+3. Non-causal softmax(Q K^T * scale) V over the whole packed sequence, one
+   softmax per query row, no padding of semantic tokens ("H3 Blackwell Runtime
+   Plan", Architecture and Non-Negotiable Validation).
+4. Optional int8 Q/K quantisation with one fp32 absmax scale per 64-token
+   block per head, and exact int32 Q K^T accumulation (the int8-QK step of the
+   SageAttention2 path: "H3 Runtime Current State", Owned Performance Kernels,
+   Q quantization and K quantization).
+
+All floating point is fp64 except where the method fixes fp32 (the int8
+quantiser, whose rounding decisions must match bit for bit).
+
+Readings where the pages are silent (each one is listed with its reason in
+the design notes of the repository):
+* RMSNorm: y = x / sqrt(mean(x^2) + eps) * gamma, eps inside the sqrt,
+  gamma of shape [d] (shared by heads) or [H, d].
+* RoPE sections are contiguous slices [0,32) t, [32,80) h, [80,128) w; inside a
+  section of width s the pairs are (j, j + s/2) for j < s/2 and the angle is
+  pos_axis * theta^(-2j/s) (the textbook RoFormer frequencies), rotating
+  (a, b) -> (a cos - b sin, b cos + a sin).
+* Int8: round-half-even, symmetric +-127, blocks of 64 tokens from token 0
+  with a partial last block, scale = fl32(absmax/127), codes =
+  rint(fl32(x * fl32(127/absmax))), an all-zero block has scale 0 and codes 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64", "f32_to_bf16_bits", "round_to_bf16",
+    "rmsnorm", "rope_layout", "rope", "prep", "prep_head",
+    "softmax_rows", "attention", "attention_head", "attention_rows_head",
+    "quantize_i8", "scores_i32", "attention_i8_rows_head",
+]
+
+
+# ----------------------------------------------------------------------------
+# bfloat16 <-> float (own converters; bf16 is the storage type of the
+# activations on the pages: "H3 Blackwell Runtime Plan", Next Performance
+# Plan keeps RMSNorm, RoPE and softmax in BF16/FP16)
+# ----------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) exactly to float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest, ties to even; NaN stays NaN."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    r[nan] = ((u[nan] >> 16).astype(np.uint16) | np.uint16(0x0040))
+    return r
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values directly to the nearest bf16 value (ties to even), as float64.
+
+    bf16 keeps 8 significant bits; below 2^-126 the spacing stays 2^-133.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                      # x = m * 2^e, 0.5 <= |m| < 1
+    quantum = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    r = np.rint(x / quantum) * quantum
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, x), r)
+    return np.where(np.isfinite(x), r, x)
+
+
+# ----------------------------------------------------------------------------
+# 1. RMSNorm per (token, head)
+# ----------------------------------------------------------------------------
+
+def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """y = x / sqrt(mean_d(x^2) + eps) * gamma over the last (head) dimension.
+
+    ``x`` is float64 [..., H, d]; ``gamma`` is [d] or [H, d].
+    """
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * gamma
+
+
+# ----------------------------------------------------------------------------
+# 2. 3-axis split-half RoPE
+# ----------------------------------------------------------------------------
+
+def rope_layout(sections) -> list:
+    """[(axis, offset, width)] of the contiguous t/h/w slices of the head dim."""
+    out, off = [], 0
+    for axis, s in enumerate(sections):
+        if s % 2:
+            raise ValueError("each RoPE section must have even width")
+        out.append((axis, off, s))
+        off += s
+    return out
+
+
+def rope(y: np.ndarray, pos: np.ndarray, sections, theta: float) -> np.ndarray:
+    """Rotate each (j, j + s/2) pair of every section by pos[axis] * theta^(-2j/s).
+
+    ``y`` float64 [N, H, d] (or [N, d]); ``pos`` integer [N, 3] in (t, h, w).
+    """
+    y = np.asarray(y, dtype=np.float64)
+    out = y.copy()
+    pos = np.asarray(pos, dtype=np.float64)
+    for axis, off, s in rope_layout(sections):
+        half = s // 2
+        j = np.arange(half, dtype=np.float64)
+        omega = theta ** (-2.0 * j / s)                       # [half]
+        phi = pos[:, axis][:, None] * omega[None, :]          # [N, half]
+        if y.ndim == 3:
+            phi = phi[:, None, :]
+        c, sn = np.cos(phi), np.sin(phi)
+        a = y[..., off:off + half]
+        b = y[..., off + half:off + s]
+        out[..., off:off + half] = a * c - b * sn
+        out[..., off + half:off + s] = b * c + a * sn
+    return out
+
+
+def prep(x_bits: np.ndarray, gamma_bits: np.ndarray, pos: np.ndarray, sections,
+         theta: float, eps: float) -> np.ndarray:
+    """RMSNorm then RoPE of bf16 [N, H, d] input; float64 [N, H, d] result."""
+    x = bf16_bits_to_f64(x_bits)
+    g = bf16_bits_to_f64(gamma_bits)
+    return rope(rmsnorm(x, g, eps), pos, sections, theta)
+
+
+def prep_head(x_bits_head: np.ndarray, gamma_bits: np.ndarray, head: int, pos: np.ndarray,
+              sections, theta: float, eps: float) -> np.ndarray:
+    """:func:`prep` of one head, from bf16 [N, d]; gamma [d] or [H, d]."""
+    g = bf16_bits_to_f64(gamma_bits)
+    if g.ndim == 2:
+        g = g[head]
+    return rope(rmsnorm(bf16_bits_to_f64(x_bits_head), g, eps), pos, sections, theta)
+
+
+# ----------------------------------------------------------------------------
+# 3. Non-causal softmax attention (exact, two-pass per query block)
+# ----------------------------------------------------------------------------
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Row softmax of a score matrix, max-subtracted (the max cancels exactly)."""
+    e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attention_rows_head(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                        block: int = 256) -> np.ndarray:
+    """O = softmax(q_rows K^T * scale) V for one head, all N keys, float64.
+
+    ``q_rows`` [R, d], ``k`` [N, d], ``v`` [N, d]; processed in query blocks of
+    ``block`` rows (each block is exact; blocking only bounds memory).
+    """
+    out = np.empty((q_rows.shape[0], v.shape[1]), dtype=np.float64)
+    for r0 in range(0, q_rows.shape[0], block):
+        s = (q_rows[r0:r0 + block] @ k.T) * scale
+        out[r0:r0 + block] = softmax_rows(s) @ v
+    return out
+
+
+def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Full attention of one head: q, k, v float64 [N, d]."""
+    return attention_rows_head(q, k, v, scale)
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Full attention over [N, H, d] float64 tensors, heads independent."""
+    out = np.empty(q.shape[:1] + (q.shape[1], v.shape[2]), dtype=np.float64)
+    for h in range(q.shape[1]):
+        out[:, h, :] = attention_head(q[:, h, :], k[:, h, :], v[:, h, :], scale)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# 4. Int8 per-64-token-block Q/K quantisation and exact int32 scores
+# ----------------------------------------------------------------------------
+
+QUANT_BLOCK = 64
+
+
+def quantize_i8(x: np.ndarray, block: int = QUANT_BLOCK):
+    """Quantise one head's [N, d] values to int8 codes with one fp32 scale per block.
+
+    ``x`` must already be float32 (the bf16-rounded prepped values).  Every
+    operation is a single IEEE float32 operation rounded to nearest even:
+    a = max|x| over the block (exact), s = a / 127, inv = 127 / a,
+    code = clamp(rint(x * inv), -127, 127); a == 0 gives s = 0 and zero codes.
+    Returns (codes int8 [N, d], scales float32 [ceil(N/block)]).
+    """
+    x = np.asarray(x)
+    if x.dtype != np.float32:
+        raise TypeError("quantize_i8 expects float32 input")
+    n = x.shape[0]
+    nb = (n + block - 1) // block
+    codes = np.zeros(x.shape, dtype=np.int8)
+    scales = np.zeros(nb, dtype=np.float32)
+    f127 = np.float32(127.0)
+    for b in range(nb):
+        xb = x[b * block:(b + 1) * block]
+        a = np.float32(np.max(np.abs(xb))) if xb.size else np.float32(0)
+        if a == 0:
+            continue
+        scales[b] = a / f127
+        inv = f127 / a
+        q = np.rint((xb * inv).astype(np.float32))
+        codes[b * block:(b + 1) * block] = np.clip(q, -127, 127).astype(np.int8)
+    return codes, scales
+
+
+def scores_i32(codes_q: np.ndarray, codes_k: np.ndarray) -> np.ndarray:
+    """Exact integer Q K^T of int8 codes, returned as int64 [R, C].
+
+    Computed as a float64 product of integer-valued matrices: every partial sum
+    is an integer of magnitude <= d * 127^2, far below 2^53, so it is exact.
+    """
+    s = codes_q.astype(np.float64) @ codes_k.astype(np.float64).T
+    return s.astype(np.int64)
+
+
+def attention_i8_rows_head(rows: np.ndarray, codes_q: np.ndarray, scales_q: np.ndarray,
+                           codes_k: np.ndarray, scales_k: np.ndarray, v: np.ndarray,
+                           scale: float, block: int = QUANT_BLOCK, qblock: int = 256) -> np.ndarray:
+    """Attention of query ``rows`` of one head from int8 Q/K codes, float64 output.
+
+    S = S_int * s_q[row block] * s_k[key block] * scale, then an exact fp64
+    softmax and P V with V float64 [N, d].
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    n = codes_k.shape[0]
+    sk = scales_k.astype(np.float64)[np.arange(n) // block]             # [N]
+    out = np.empty((rows.size, v.shape[1]), dtype=np.float64)
+    for r0 in range(0, rows.size, qblock):
+        rr = rows[r0:r0 + qblock]
+        s_int = scores_i32(codes_q[rr], codes_k).astype(np.float64)
+        sq = scales_q.astype(np.float64)[rr // block]
+        s = s_int * sq[:, None] * sk[None, :] * scale
+        out[r0:r0 + qblock] = softmax_rows(s) @ v
+    return out
