@@ -1,0 +1,60 @@
+"""Build ``libh3attn.so`` (gfx950 kernels + C ABI) in-tree with hipcc.
+
+    python -m audio_video_diffusion_amd.build          # compile
+    python -m audio_video_diffusion_amd.build --asm     # also keep the gfx950 assembly
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libh3attn.so")
+SOURCES = ("api.hip", "prep.hip", "forward.hip")
+ARCH = "gfx950"
+
+# Packed fp32 VALU forms are kept out of the generated code.  No fast-math: the
+# int8 quantiser relies on correctly rounded fp32 division.
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build libh3attn.so")
+
+
+def build(verbose: bool = False, asm: bool = False) -> str:
+    """Compile every HIP source into the in-tree shared library; returns its path."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+    if asm:
+        os.makedirs(os.path.join(ROOT, "_build"), exist_ok=True)
+        cmd[1:1] = ["-save-temps=obj"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    cwd = os.path.join(ROOT, "_build") if asm else CSRC
+    res = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
+    # the host pass warns that it does not know the packed-fp32 feature: harmless
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
+            if "packed-fp32-ops" not in ln and ln.strip()]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True, asm="--asm" in sys.argv))

@@ -1,0 +1,229 @@
+// C ABI of the packed-attention library: argument validation and launches.
+//
+// Every check runs on the host before anything is enqueued, so a rejected
+// call has no side effect.  The library keeps no state, never allocates and
+// never synchronises.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/h3attn.h"
+#include "params.h"
+
+
+namespace {
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;   // keeps every int32 index in range
+
+struct Range {
+    uintptr_t lo, hi;    // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Byte extent of a strided [N][H][d] view.
+Range view_range(const void* p, int64_t n, int64_t h, int64_t st, int64_t sh, int64_t d, int64_t elt) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return {b, b + (uintptr_t)(((n - 1) * st + (h - 1) * sh + d) * elt)};
+}
+Range span(const void* p, size_t bytes) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return {b, b + bytes};
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_problem(const h3attn_problem* p) {
+    if (!p) return H3ATTN_E_NULL;
+    if (p->head_dim != 128) return H3ATTN_E_UNSUPPORTED;
+    if (p->qk_format != H3ATTN_QK_BF16 && p->qk_format != H3ATTN_QK_I8_BLK64) return H3ATTN_E_UNSUPPORTED;
+    if (p->n_tokens < 1 || p->n_tokens > kMaxTokens || p->n_heads < 1) return H3ATTN_E_SHAPE;
+    // the head-major prepped tensors are indexed with 64-bit offsets, but keep H*N_pad*d sane
+    const int64_t npad = ((int64_t)p->n_tokens + 255) / 256 * 256;
+    if ((int64_t)p->n_heads * npad > ((int64_t)1 << 40)) return H3ATTN_E_SHAPE;
+    int sum = 0;
+    for (int a = 0; a < 3; ++a) {
+        const int s = p->rope_sections[a];
+        if (s < 0) return H3ATTN_E_SHAPE;
+        if (s % 16) return H3ATTN_E_UNSUPPORTED;
+        sum += s;
+    }
+    if (sum != p->head_dim) return H3ATTN_E_SHAPE;
+    if (!(p->rope_theta > 0.f) || !isfinite(p->rope_theta)) return H3ATTN_E_SHAPE;
+    if (!(p->rms_eps >= 0.f) || !isfinite(p->rms_eps)) return H3ATTN_E_SHAPE;
+    return H3ATTN_OK;
+}
+
+int64_t npad_of(const h3attn_problem* p) { return ((int64_t)p->n_tokens + 255) / 256 * 256; }
+int64_t nblk_of(const h3attn_problem* p) { return ((int64_t)p->n_tokens + 63) / 64; }
+
+// strides of an input view: non-negative multiples of 8 elements
+int check_in_view(const void* ptr, int64_t st, int64_t sh) {
+    if (!ptr) return H3ATTN_E_NULL;
+    if (st < 0 || sh < 0) return H3ATTN_E_SHAPE;
+    if (!aligned(ptr, 16) || (st % 8) || (sh % 8)) return H3ATTN_E_ALIGN;
+    return H3ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int h3attn_abi_version(void) { return H3ATTN_ABI_VERSION; }
+
+const char* h3attn_status_string(int s) {
+    switch (s) {
+        case H3ATTN_OK: return "ok";
+        case H3ATTN_E_NULL: return "a required pointer is NULL";
+        case H3ATTN_E_SHAPE: return "invalid shape, stride, window or scalar argument";
+        case H3ATTN_E_UNSUPPORTED: return "unsupported head_dim, format or RoPE section widths";
+        case H3ATTN_E_ALIGN: return "pointer or stride misaligned";
+        case H3ATTN_E_ALIAS: return "an output overlaps another buffer";
+        case H3ATTN_E_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int64_t h3attn_padded_tokens(const h3attn_problem* p) {
+    return check_problem(p) == H3ATTN_OK ? npad_of(p) : 0;
+}
+
+size_t h3attn_prepped_qk_bytes(const h3attn_problem* p) {
+    if (check_problem(p) != H3ATTN_OK) return 0;
+    const size_t elt = p->qk_format == H3ATTN_QK_BF16 ? 2 : 1;
+    return (size_t)p->n_heads * (size_t)npad_of(p) * 128 * elt;
+}
+
+size_t h3attn_scales_bytes(const h3attn_problem* p) {
+    if (check_problem(p) != H3ATTN_OK || p->qk_format != H3ATTN_QK_I8_BLK64) return 0;
+    return (size_t)p->n_heads * (size_t)nblk_of(p) * sizeof(float);
+}
+
+int h3attn_prep(const h3attn_problem* p,
+                const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                const void* gamma_q, const void* gamma_k, int64_t gamma_head_stride,
+                const int32_t* pos_thw,
+                void* q_out, void* k_out, float* q_scales, float* k_scales,
+                void* stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    const bool i8 = p->qk_format == H3ATTN_QK_I8_BLK64;
+    if ((rc = check_in_view(q, q_stride_tok, q_stride_head))) return rc;
+    if ((rc = check_in_view(k, k_stride_tok, k_stride_head))) return rc;
+    if ((rc = check_in_view(gamma_q, 0, gamma_head_stride))) return rc;
+    if ((rc = check_in_view(gamma_k, 0, gamma_head_stride))) return rc;
+    if (!pos_thw || !q_out || !k_out) return H3ATTN_E_NULL;
+    if (i8 && (!q_scales || !k_scales)) return H3ATTN_E_NULL;
+    if (!i8 && (q_scales || k_scales)) return H3ATTN_E_SHAPE;
+    if (!aligned(pos_thw, 4) || !aligned(q_out, 16) || !aligned(k_out, 16)) return H3ATTN_E_ALIGN;
+    if (i8 && (!aligned(q_scales, 4) || !aligned(k_scales, 4))) return H3ATTN_E_ALIGN;
+
+    const int64_t n = p->n_tokens, h = p->n_heads;
+    const size_t out_b = h3attn_prepped_qk_bytes(p), sc_b = h3attn_scales_bytes(p);
+    const Range ins[5] = {view_range(q, n, h, q_stride_tok, q_stride_head, 128, 2),
+                          view_range(k, n, h, k_stride_tok, k_stride_head, 128, 2),
+                          view_range(gamma_q, 1, h, 0, gamma_head_stride, 128, 2),
+                          view_range(gamma_k, 1, h, 0, gamma_head_stride, 128, 2),
+                          span(pos_thw, (size_t)n * 3 * sizeof(int32_t))};
+    Range outs[4] = {span(q_out, out_b), span(k_out, out_b), {0, 0}, {0, 0}};
+    const int nout = i8 ? 4 : 2;
+    if (i8) {
+        outs[2] = span(q_scales, sc_b);
+        outs[3] = span(k_scales, sc_b);
+    }
+    for (int o = 0; o < nout; ++o) {
+        for (const Range& r : ins)
+            if (overlap(outs[o], r)) return H3ATTN_E_ALIAS;
+        for (int o2 = o + 1; o2 < nout; ++o2)
+            if (overlap(outs[o], outs[o2])) return H3ATTN_E_ALIAS;
+    }
+
+    h3::PrepParams P{};
+    P.q = static_cast<const uint16_t*>(q); P.q_st = q_stride_tok; P.q_sh = q_stride_head;
+    P.k = static_cast<const uint16_t*>(k); P.k_st = k_stride_tok; P.k_sh = k_stride_head;
+    P.gq = static_cast<const uint16_t*>(gamma_q); P.gk = static_cast<const uint16_t*>(gamma_k);
+    P.g_sh = gamma_head_stride;
+    P.pos = pos_thw;
+    P.q_out = q_out; P.k_out = k_out; P.q_scales = q_scales; P.k_scales = k_scales;
+    P.n = (int)n; P.h = (int)h; P.npad = (int)npad_of(p); P.nblk = (int)nblk_of(p);
+    P.theta = p->rope_theta; P.eps = p->rms_eps;
+    P.sec0 = p->rope_sections[0]; P.sec1 = p->rope_sections[1]; P.sec2 = p->rope_sections[2];
+    if (h3::launch_prep(P, i8, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
+    return H3ATTN_OK;
+}
+
+int h3attn_forward(const h3attn_problem* p,
+                   const void* q_prep, const void* k_prep,
+                   const float* q_scales, const float* k_scales,
+                   const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                   void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                   float softmax_scale, void* stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    const bool i8 = p->qk_format == H3ATTN_QK_I8_BLK64;
+    if (!q_prep || !k_prep) return H3ATTN_E_NULL;
+    if (!aligned(q_prep, 16) || !aligned(k_prep, 16)) return H3ATTN_E_ALIGN;
+    if (i8 && (!q_scales || !k_scales)) return H3ATTN_E_NULL;
+    if (!i8 && (q_scales || k_scales)) return H3ATTN_E_SHAPE;
+    if (i8 && (!aligned(q_scales, 4) || !aligned(k_scales, 4))) return H3ATTN_E_ALIGN;
+    if ((rc = check_in_view(v, v_stride_tok, v_stride_head))) return rc;
+    if ((rc = check_in_view(o, o_stride_tok, o_stride_head))) return rc;
+    if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return H3ATTN_E_SHAPE;
+
+    const int64_t n = p->n_tokens, h = p->n_heads;
+    // the output view must not overlap itself
+    const bool nhd_ok = o_stride_head >= 128 && o_stride_tok >= (h - 1) * o_stride_head + 128;
+    const bool hnd_ok = o_stride_tok >= 128 && o_stride_head >= (n - 1) * o_stride_tok + 128;
+    if (!(nhd_ok || hnd_ok)) return H3ATTN_E_SHAPE;
+
+    const size_t in_b = h3attn_prepped_qk_bytes(p), sc_b = h3attn_scales_bytes(p);
+    const Range orng = view_range(o, n, h, o_stride_tok, o_stride_head, 128, 2);
+    if (overlap(orng, span(q_prep, in_b)) || overlap(orng, span(k_prep, in_b)) ||
+        overlap(orng, view_range(v, n, h, v_stride_tok, v_stride_head, 128, 2)))
+        return H3ATTN_E_ALIAS;
+    if (i8 && (overlap(orng, span(q_scales, sc_b)) || overlap(orng, span(k_scales, sc_b))))
+        return H3ATTN_E_ALIAS;
+
+    h3::FwdParams P{};
+    P.q = q_prep; P.k = k_prep; P.qs = q_scales; P.ks = k_scales;
+    P.v = static_cast<const uint16_t*>(v); P.v_st = v_stride_tok; P.v_sh = v_stride_head;
+    P.o = static_cast<uint16_t*>(o); P.o_st = o_stride_tok; P.o_sh = o_stride_head;
+    P.n = (int)n; P.h = (int)h; P.npad = (int)npad_of(p); P.nblk = (int)nblk_of(p);
+    P.qtiles = (int)((n + 255) / 256);
+    const int64_t total = h * P.qtiles;
+    if (total > ((int64_t)1 << 28)) return H3ATTN_E_SHAPE;
+    P.total = (int)total;
+    P.per_xcd = (int)((total + 7) / 8);
+    P.c = (float)((double)softmax_scale * 1.4426950408889634);
+    if (h3::launch_forward(P, i8, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
+    return H3ATTN_OK;
+}
+
+int h3attn_debug_scores_i32(const h3attn_problem* p, const void* q_codes, const void* k_codes,
+                            int32_t head, int32_t row0, int32_t nrows, int32_t col0, int32_t ncols,
+                            int32_t* out, void* stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if (p->qk_format != H3ATTN_QK_I8_BLK64) return H3ATTN_E_UNSUPPORTED;
+    if (!q_codes || !k_codes || !out) return H3ATTN_E_NULL;
+    if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(out, 4)) return H3ATTN_E_ALIGN;
+    const int64_t n = p->n_tokens;
+    if (head < 0 || head >= p->n_heads || nrows < 1 || ncols < 1 || row0 < 0 || col0 < 0 ||
+        (int64_t)row0 + nrows > n || (int64_t)col0 + ncols > n)
+        return H3ATTN_E_SHAPE;
+    const size_t in_b = h3attn_prepped_qk_bytes(p);
+    const Range orng = span(out, (size_t)nrows * (size_t)ncols * sizeof(int32_t));
+    if (overlap(orng, span(q_codes, in_b)) || overlap(orng, span(k_codes, in_b))) return H3ATTN_E_ALIAS;
+
+    h3::ScoreParams P{};
+    const int64_t head_off = (int64_t)head * npad_of(p) * 128;
+    P.qhead = static_cast<const uint8_t*>(q_codes) + head_off;
+    P.khead = static_cast<const uint8_t*>(k_codes) + head_off;
+    P.n = (int)n; P.npad = (int)npad_of(p);
+    P.row0 = row0; P.nrows = nrows; P.col0 = col0; P.ncols = ncols;
+    P.out = out;
+    if (h3::launch_scores_i8(P, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
+    return H3ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Launch parameters of the gfx950 kernels (shared by the C-ABI layer and the kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3 {
+
+struct PrepParams {
+    const uint16_t* q; int64_t q_st, q_sh;      // bf16 NHD views (element strides)
+    const uint16_t* k; int64_t k_st, k_sh;
+    const uint16_t* gq; const uint16_t* gk; int64_t g_sh;
+    const int32_t* pos;                          // [N][3]
+    void* q_out; void* k_out;                    // [H][npad][128] bf16 or int8
+    float* q_scales; float* k_scales;            // [H][nblk] (int8 only)
+    int n, h, npad, nblk;
+    float theta, eps;
+    int sec0, sec1, sec2;
+};
+
+struct FwdParams {
+    const void* q;          // [H][npad][128] bf16 or int8
+    const void* k;
+    const float* qs;        // [H][nblk] (int8 only)
+    const float* ks;
+    const uint16_t* v; int64_t v_st, v_sh;
+    uint16_t* o; int64_t o_st, o_sh;
+    int n, h, npad, nblk;
+    int qtiles;             // ceil(N / 256)
+    int total;              // H * qtiles
+    int per_xcd;            // ceil(total / 8)
+    float c;                // softmax_scale * log2(e)
+};
+
+struct ScoreParams {
+    const uint8_t* qhead;   // head base of the int8 codes
+    const uint8_t* khead;
+    int n, npad;
+    int row0, nrows, col0, ncols;
+    int32_t* out;
+};
+
+hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream);
+hipError_t launch_forward(const FwdParams& P, bool int8, hipStream_t stream);
+hipError_t launch_scores_i8(const ScoreParams& P, hipStream_t stream);
+
+}  // namespace h3

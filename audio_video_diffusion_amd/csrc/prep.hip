@@ -1,0 +1,246 @@
+// Q/K RMSNorm + 3-axis split-half RoPE + head-major layout (+ optional int8 block
+// quantisation) for gfx950.
+//
+// What is computed is the entry step of the packed-attention block: per-head
+// RMSNorm then split-half RoPE of strided-NHD Q and K ("H3 Runtime Current
+// State", Owned Performance Kernels: the fused entry kernel; "H3 Blackwell
+// Runtime Plan", 2026-08-15 Handoff: fused Q/K RMS + RoPE + HND layout), with
+// the int8 Q/K quantisation of the quantised attention path as an option
+// ("H3 Runtime Current State", Owned Performance Kernels: Q quantization,
+// K quantization).
+//
+// The step is HBM-bound (read Q and K once, write Q' and K' once).  Mapping:
+// one 256-thread work-group owns a 64-token block for ALL heads.  Eight
+// threads own one token row of a head: thread slot p holds the 16-byte chunk
+// a(p) of the first half of a RoPE section and its partner chunk b(p) of the
+// second half, so the rotation is thread-local and only the sum of squares
+// is reduced across the eight lanes.  cos/sin of the thread's 8 angles are
+// computed once per token and reused for every head and for both Q and K.
+// The 64-token block is exactly one int8 scale block, so the block absmax is a
+// work-group reduction.
+#include "common.h"
+#include "params.h"
+
+namespace h3 {
+
+
+struct Slot {
+    int a, b;       // chunk index (of 16) of the first-half chunk and its partner
+    int axis;       // 0 = t, 1 = h, 2 = w
+    int j0;         // frequency index of element 0 of chunk a inside its section
+    int width;      // section width s
+};
+
+__device__ __forceinline__ Slot slot_of(int p, int s0, int s1, int s2) {
+    const int w[3] = {s0, s1, s2};
+    int off = 0;
+    Slot r{0, 0, 0, 0, 16};
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) {
+        const int cnt = w[ax] / 16;          // first-half chunks of this section
+        if (p >= 0 && p < cnt) {
+            r.a = off / 8 + p;
+            r.b = r.a + cnt;
+            r.axis = ax;
+            r.j0 = 8 * p;
+            r.width = w[ax];
+        }
+        p -= cnt;
+        off += w[ax];
+    }
+    return r;
+}
+
+__device__ __forceinline__ void unpack8(u32x4 v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16lo_to_f32(v[i]);
+        f[2 * i + 1] = bf16hi_to_f32(v[i]);
+    }
+}
+
+__device__ __forceinline__ float sum8lanes(float v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    return v;
+}
+
+// RMSNorm + rotation of one (token, head) pair of chunks; result rounded to bf16
+// and returned both as packed words and as the rounded fp32 values.
+__device__ __forceinline__ void norm_rotate(const float* xa, const float* xb, const float* ga,
+                                            const float* gb, const float* cs, const float* sn,
+                                            float eps, u32x4& oa, u32x4& ob, float* ra, float* rb) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += xa[i] * xa[i] + xb[i] * xb[i];
+    ss = sum8lanes(ss);
+    const float rinv = rsqrtf(ss * (1.0f / kHeadDim) + eps);
+    float ya[8], yb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float u = xa[i] * rinv * ga[i];
+        const float w = xb[i] * rinv * gb[i];
+        ya[i] = u * cs[i] - w * sn[i];
+        yb[i] = w * cs[i] + u * sn[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        oa[i] = pack_bf16x2(ya[2 * i], ya[2 * i + 1]);
+        ob[i] = pack_bf16x2(yb[2 * i], yb[2 * i + 1]);
+        ra[2 * i] = bf16lo_to_f32(oa[i]);
+        ra[2 * i + 1] = bf16hi_to_f32(oa[i]);
+        rb[2 * i] = bf16lo_to_f32(ob[i]);
+        rb[2 * i + 1] = bf16hi_to_f32(ob[i]);
+    }
+}
+
+__device__ __forceinline__ uint32_t quant4(const float* v, float inv) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float c = __builtin_rintf(v[i] * inv);
+        c = fminf(fmaxf(c, -127.f), 127.f);
+        w |= (uint32_t)((int)c & 0xff) << (8 * i);
+    }
+    return w;
+}
+
+template <bool kInt8>
+__global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
+    const int tid = threadIdx.x;
+    const int row = tid >> 3;            // 0..31
+    const int p = tid & 7;               // slot
+    const int t0 = blockIdx.x * 64;
+    const Slot sl = slot_of(p, P.sec0, P.sec1, P.sec2);
+
+    int tok[2];
+    bool valid[2];
+    float cs[2][8], sn[2][8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        tok[t] = t0 + row + 32 * t;
+        valid[t] = tok[t] < P.n;
+        const float pv = valid[t] ? (float)P.pos[(int64_t)tok[t] * 3 + sl.axis] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float j = (float)(sl.j0 + i);
+            const float omega = powf(P.theta, -2.0f * j / (float)sl.width);
+            sincosf(pv * omega, &sn[t][i], &cs[t][i]);
+        }
+    }
+
+    float gqa[8], gqb[8], gka[8], gkb[8];
+    auto load_gamma = [&](int h) {
+        unpack8(ld16(P.gq + h * P.g_sh + 8 * sl.a), gqa);
+        unpack8(ld16(P.gq + h * P.g_sh + 8 * sl.b), gqb);
+        unpack8(ld16(P.gk + h * P.g_sh + 8 * sl.a), gka);
+        unpack8(ld16(P.gk + h * P.g_sh + 8 * sl.b), gkb);
+    };
+    load_gamma(0);
+
+    __shared__ float red[2][2][4];      // [head parity][q/k][wave]
+    const int wave = tid >> 6;
+
+    for (int h = 0; h < P.h; ++h) {
+        if (P.g_sh != 0 && h > 0) load_gamma(h);
+        u32x4 qa[2], qb[2], ka[2], kb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (valid[t]) {
+                const uint16_t* qr = P.q + (int64_t)tok[t] * P.q_st + (int64_t)h * P.q_sh;
+                const uint16_t* kr = P.k + (int64_t)tok[t] * P.k_st + (int64_t)h * P.k_sh;
+                qa[t] = ld16(qr + 8 * sl.a);
+                qb[t] = ld16(qr + 8 * sl.b);
+                ka[t] = ld16(kr + 8 * sl.a);
+                kb[t] = ld16(kr + 8 * sl.b);
+            } else {
+                qa[t] = qb[t] = ka[t] = kb[t] = u32x4{0, 0, 0, 0};
+            }
+        }
+        float rq[2][16], rk[2][16];
+        u32x4 oqa[2], oqb[2], oka[2], okb[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            float xa[8], xb[8];
+            unpack8(qa[t], xa);
+            unpack8(qb[t], xb);
+            norm_rotate(xa, xb, gqa, gqb, cs[t], sn[t], P.eps, oqa[t], oqb[t], rq[t], rq[t] + 8);
+            unpack8(ka[t], xa);
+            unpack8(kb[t], xb);
+            norm_rotate(xa, xb, gka, gkb, cs[t], sn[t], P.eps, oka[t], okb[t], rk[t], rk[t] + 8);
+            if (!valid[t]) {
+                oqa[t] = oqb[t] = oka[t] = okb[t] = u32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int i = 0; i < 16; ++i) rq[t][i] = rk[t][i] = 0.f;
+            }
+        }
+        const int64_t head_base = (int64_t)h * P.npad;
+        if constexpr (!kInt8) {
+            uint16_t* qo = static_cast<uint16_t*>(P.q_out);
+            uint16_t* ko = static_cast<uint16_t*>(P.k_out);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int64_t r = (head_base + tok[t]) * kHeadDim;
+                st16(qo + r + 8 * sl.a, oqa[t]);
+                st16(qo + r + 8 * sl.b, oqb[t]);
+                st16(ko + r + 8 * sl.a, oka[t]);
+                st16(ko + r + 8 * sl.b, okb[t]);
+            }
+        } else {
+            float mq = 0.f, mk = 0.f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    mq = fmaxf(mq, fabsf(rq[t][i]));
+                    mk = fmaxf(mk, fabsf(rk[t][i]));
+                }
+#pragma unroll
+            for (int s = 1; s < 64; s <<= 1) {
+                mq = fmaxf(mq, __shfl_xor(mq, s));
+                mk = fmaxf(mk, __shfl_xor(mk, s));
+            }
+            if ((tid & 63) == 0) {
+                red[h & 1][0][wave] = mq;
+                red[h & 1][1][wave] = mk;
+            }
+            __syncthreads();
+            float aq = red[h & 1][0][0], ak = red[h & 1][1][0];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) {
+                aq = fmaxf(aq, red[h & 1][0][w]);
+                ak = fmaxf(ak, red[h & 1][1][w]);
+            }
+            // IEEE fp32 divisions (correctly rounded: no fast-math in this build)
+            const float sq = aq / 127.0f, sk = ak / 127.0f;
+            const float iq = aq > 0.f ? 127.0f / aq : 0.f;
+            const float ik = ak > 0.f ? 127.0f / ak : 0.f;
+            if (tid == 0 && t0 < P.n) {
+                P.q_scales[(int64_t)h * P.nblk + blockIdx.x] = sq;
+                P.k_scales[(int64_t)h * P.nblk + blockIdx.x] = sk;
+            }
+            int8_t* qo = static_cast<int8_t*>(P.q_out);
+            int8_t* ko = static_cast<int8_t*>(P.k_out);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int64_t r = (head_base + tok[t]) * kHeadDim;
+                st8(qo + r + 8 * sl.a, u32x2{quant4(rq[t], iq), quant4(rq[t] + 4, iq)});
+                st8(qo + r + 8 * sl.b, u32x2{quant4(rq[t] + 8, iq), quant4(rq[t] + 12, iq)});
+                st8(ko + r + 8 * sl.a, u32x2{quant4(rk[t], ik), quant4(rk[t] + 4, ik)});
+                st8(ko + r + 8 * sl.b, u32x2{quant4(rk[t] + 8, ik), quant4(rk[t] + 12, ik)});
+            }
+        }
+    }
+}
+
+hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream) {
+    dim3 grid(P.npad / 64), block(256);
+    if (int8)
+        hipLaunchKernelGGL(prep_kernel<true>, grid, block, 0, stream, P);
+    else
+        hipLaunchKernelGGL(prep_kernel<false>, grid, block, 0, stream, P);
+    return hipGetLastError();
+}
+
+}  // namespace h3

@@ -1,0 +1,166 @@
+"""Thin Python binding of ``libh3attn.so`` (argument marshalling only).
+
+Every step of the path runs in the library's HIP kernels; this module only
+turns torch tensors into pointers, strides and a stream handle.  There is no
+fallback: if the library is not built, importing the binding raises.
+
+The calls mirror ``include/h3attn.h``:
+
+* :func:`prep`      - Q/K RMSNorm + 3-axis split-half RoPE -> head-major Q'/K'
+* :func:`forward`   - softmax(Q' K'^T * scale) V over the packed sequence
+* :func:`debug_scores_i32` - exact int32 Q'K'^T window of the int8 format
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libh3attn.so")
+
+QK_BF16 = 0
+QK_I8_BLK64 = 1
+ABI_VERSION = 1
+
+STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_UNSUPPORTED", -4: "E_ALIGN",
+          -5: "E_ALIAS", -6: "E_HIP"}
+
+
+class H3AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {STATUS.get(status, status)} ({_lib.h3attn_status_string(status).decode()})")
+
+
+class Problem(ctypes.Structure):
+    """``h3attn_problem`` (host memory)."""
+    _fields_ = [
+        ("n_tokens", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rope_sections", ctypes.c_int32 * 3),
+        ("rope_theta", ctypes.c_float),
+        ("rms_eps", ctypes.c_float),
+        ("qk_format", ctypes.c_int32),
+    ]
+
+
+def problem(n_tokens: int, n_heads: int, qk_format: int = QK_BF16, head_dim: int = 128,
+            sections=(32, 48, 48), theta: float = 10000.0, eps: float = 1e-6) -> Problem:
+    p = Problem()
+    p.n_tokens, p.n_heads, p.head_dim = n_tokens, n_heads, head_dim
+    p.rope_sections[:] = list(sections)
+    p.rope_theta, p.rms_eps, p.qk_format = theta, eps, qk_format
+    return p
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m audio_video_diffusion_amd.build` "
+                          "(the HIP library is required; there is no fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    pp = ctypes.POINTER(Problem)
+    sig = {
+        "h3attn_abi_version": (ctypes.c_int, []),
+        "h3attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "h3attn_padded_tokens": (i64, [pp]),
+        "h3attn_prepped_qk_bytes": (ctypes.c_size_t, [pp]),
+        "h3attn_scales_bytes": (ctypes.c_size_t, [pp]),
+        "h3attn_prep": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, i64, vp, vp, i64, vp,
+                                       vp, vp, vp, vp, vp]),
+        "h3attn_forward": (ctypes.c_int, [pp, vp, vp, vp, vp, vp, i64, i64, vp, i64, i64, f32, vp]),
+        "h3attn_debug_scores_i32": (ctypes.c_int, [pp, vp, vp, i32, i32, i32, i32, i32, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    if lib.h3attn_abi_version() != ABI_VERSION:
+        raise ImportError("libh3attn.so ABI version mismatch: rebuild it")
+    return lib
+
+
+_lib = _load()
+lib = _lib
+
+
+def padded_tokens(p: Problem) -> int:
+    return _lib.h3attn_padded_tokens(ctypes.byref(p))
+
+
+def prepped_qk_bytes(p: Problem) -> int:
+    return _lib.h3attn_prepped_qk_bytes(ctypes.byref(p))
+
+
+def scales_bytes(p: Problem) -> int:
+    return _lib.h3attn_scales_bytes(ctypes.byref(p))
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _nhd(t, name):
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be an [N, H, d] view with a contiguous last axis")
+    return t.data_ptr(), t.stride(0), t.stride(1)
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def alloc_prepped(p: Problem, device="cuda"):
+    """Caller-side buffers for :func:`prep`: (q_out, k_out, q_scales, k_scales)."""
+    import torch
+    npad = padded_tokens(p)
+    dt = torch.bfloat16 if p.qk_format == QK_BF16 else torch.int8
+    q_out = torch.empty((p.n_heads, npad, p.head_dim), dtype=dt, device=device)
+    k_out = torch.empty_like(q_out)
+    if p.qk_format == QK_BF16:
+        return q_out, k_out, None, None
+    nblk = (p.n_tokens + 63) // 64
+    q_s = torch.empty((p.n_heads, nblk), dtype=torch.float32, device=device)
+    return q_out, k_out, q_s, torch.empty_like(q_s)
+
+
+def prep(p: Problem, q, k, gamma_q, gamma_k, pos, q_out, k_out, q_scales=None, k_scales=None,
+         stream=None):
+    """``h3attn_prep`` on torch tensors (bf16 q/k views [N,H,d], gamma [d] or [H,d], pos int32 [N,3])."""
+    qp, qst, qsh = _nhd(q, "q")
+    kp, kst, ksh = _nhd(k, "k")
+    if gamma_q.shape != gamma_k.shape or gamma_q.stride() != gamma_k.stride():
+        raise ValueError("gamma_q and gamma_k must have the same shape and strides")
+    gsh = gamma_q.stride(0) if gamma_q.dim() == 2 else 0
+    rc = _lib.h3attn_prep(ctypes.byref(p), qp, qst, qsh, kp, kst, ksh, _ptr(gamma_q), _ptr(gamma_k),
+                          gsh, _ptr(pos), _ptr(q_out), _ptr(k_out), _ptr(q_scales), _ptr(k_scales),
+                          _stream(stream))
+    if rc:
+        raise H3AttnError(rc, "h3attn_prep")
+
+
+def forward(p: Problem, q_prep, k_prep, v, o, softmax_scale: float, q_scales=None, k_scales=None,
+            stream=None):
+    """``h3attn_forward`` on torch tensors (v and o bf16 [N,H,d] views)."""
+    vp, vst, vsh = _nhd(v, "v")
+    op, ost, osh = _nhd(o, "o")
+    rc = _lib.h3attn_forward(ctypes.byref(p), _ptr(q_prep), _ptr(k_prep), _ptr(q_scales),
+                             _ptr(k_scales), vp, vst, vsh, op, ost, osh, float(softmax_scale),
+                             _stream(stream))
+    if rc:
+        raise H3AttnError(rc, "h3attn_forward")
+
+
+def debug_scores_i32(p: Problem, q_codes, k_codes, head: int, row0: int, nrows: int, col0: int,
+                     ncols: int, out, stream=None):
+    """``h3attn_debug_scores_i32`` into ``out`` (int32 [nrows, ncols], contiguous)."""
+    rc = _lib.h3attn_debug_scores_i32(ctypes.byref(p), _ptr(q_codes), _ptr(k_codes), head, row0,
+                                      nrows, col0, ncols, _ptr(out), _stream(stream))
+    if rc:
+        raise H3AttnError(rc, "h3attn_debug_scores_i32")

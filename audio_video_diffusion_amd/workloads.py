@@ -164,3 +164,27 @@ def ragged_workload(n: int, heads: int) -> Workload:
     audio = min(n - text, 5)
     video = n - text - audio
     return Workload(f"ragged_{n}", (1, 1, video), audio, text, heads)
+
+
+def bits_to_torch(bits: np.ndarray, device="cuda"):
+    """uint16 bf16 bit patterns -> torch.bfloat16 tensor on ``device`` (same shape)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to(device)
+
+
+def torch_to_bits(t) -> np.ndarray:
+    """torch.bfloat16 tensor (any device) -> uint16 bit patterns on the host."""
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def device_inputs(inp: Inputs, device="cuda") -> dict:
+    """Upload an :class:`Inputs` to ``device`` as torch tensors."""
+    import torch
+    return {
+        "q": bits_to_torch(inp.q, device), "k": bits_to_torch(inp.k, device),
+        "v": bits_to_torch(inp.v, device),
+        "gamma_q": bits_to_torch(inp.gamma_q, device), "gamma_k": bits_to_torch(inp.gamma_k, device),
+        "pos": torch.from_numpy(inp.pos).to(device),
+    }

@@ -1,0 +1,173 @@
+#!/usr/bin/env python3
+"""Throughput of the packed-attention hot path on one MI355X.
+
+One step = h3attn_prep (Q/K RMSNorm + 3-axis RoPE + head-major layout) then
+h3attn_forward (non-causal attention over the whole packed sequence) on one
+batch of seeded synthetic inputs already resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+
+Prints one JSON line.  ``value`` is attention TFLOP/s (4 N^2 d H per step)
+over the whole step; ``roofline`` rates the forward kernel alone against the
+bf16 matrix-core peak; ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
+PEAK_INT8_TOPS = 5033.2
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=None, help="workload index (default: the 129,410-token one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, cfg, inp, rows_n, heads_n):
+    """Time the CPU oracle on `rows_n` query rows x `heads_n` heads of the workload."""
+    import numpy as np
+    import oracle as O
+    from audio_video_diffusion_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    n = wl.n_tokens
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(n, size=min(rows_n, n), replace=False))
+    heads = list(range(min(heads_n, wl.heads)))
+    scale = 1.0 / math.sqrt(128.0)
+    sec, th, eps = W.ROPE_SECTIONS, W.ROPE_THETA, W.RMS_EPS
+    t0 = time.perf_counter()
+    for h in heads:
+        kp = O.prep_head(inp.k[:, h, :], inp.gamma_k, h, inp.pos, sec, th, eps)
+        v = O.bf16_bits_to_f64(inp.v[:, h, :])
+        if wl.qk_int8:
+            qp = O.prep_head(inp.q[:, h, :], inp.gamma_q, h, inp.pos, sec, th, eps)
+            cq, sq = O.quantize_i8(O.round_to_bf16(qp).astype(np.float32))
+            ck, sk = O.quantize_i8(O.round_to_bf16(kp).astype(np.float32))
+            O.attention_i8_rows_head(rows, cq, sq, ck, sk, v, scale)
+        else:
+            qp = O.prep_head(inp.q[rows, h, :], inp.gamma_q, h, inp.pos[rows], sec, th, eps)
+            O.attention_rows_head(qp, kp, v, scale)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * len(rows) * n * 128 * len(heads)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} random query rows x {len(heads)} heads of {wl.name} (all {n} keys, "
+                      f"prep of every key included), fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the path has no "
+              "multi-GPU mode; heads would shard across GPUs with an all-to-all, which is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from audio_video_diffusion_amd import h3attn as A
+    from audio_video_diffusion_amd import workloads as W
+
+    cfg = W.HEADLINE if args.config is None else args.config
+    wl = W.WORKLOADS[cfg]
+    print(f"[bench] generating {wl.name}: N={wl.n_tokens} H={wl.heads}", file=sys.stderr, flush=True)
+    inp = W.make_inputs(cfg, threads=16)
+    dev = W.device_inputs(inp)
+    fmt = A.QK_I8_BLK64 if wl.qk_int8 else A.QK_BF16
+    p = A.problem(wl.n_tokens, wl.heads, fmt)
+    q_out, k_out, qs, ks = A.alloc_prepped(p)
+    o = torch.empty_like(dev["v"])
+    scale = 1.0 / math.sqrt(128.0)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(timed=None):
+        if timed is not None:
+            e0, e1, e2 = ev(), ev(), ev()
+            e0.record()
+        A.prep(p, dev["q"], dev["k"], dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
+        if timed is not None:
+            e1.record()
+        A.forward(p, q_out, k_out, dev["v"], o, scale, qs, ks)
+        if timed is not None:
+            e2.record()
+            timed.append((e0, e1, e2))
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    timed = []
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t_start = ev()
+    t_end = ev()
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step(timed)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    prep_ms = sum(a.elapsed_time(b) for a, b, _ in timed) / len(timed)
+    fwd_ms = sum(b.elapsed_time(c) for _, b, c in timed) / len(timed)
+
+    flops = wl.flops
+    value = flops / (ms_step * 1e-3) / 1e12
+    fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
+    peak = PEAK_INT8_TOPS if wl.qk_int8 else PEAK_BF16_TFLOPS
+    # prep: algorithmic bytes = read Q and K (bf16), write Q' and K' (+ scales in int8)
+    n, h = wl.n_tokens, wl.heads
+    prep_bytes = 2 * n * h * 128 * 2 + 2 * n * h * 128 * (1 if wl.qk_int8 else 2) + \
+        (2 * h * ((n + 63) // 64) * 4 if wl.qk_int8 else 0)
+
+    res = {
+        "metric": "attention TFLOP/s and % bf16 MFMA peak at 129k packed tokens, 24 heads, d=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8-qk/bf16-pv" if wl.qk_int8 else "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, gamma ~ N(1,0.1))",
+        "config": {"workload": wl.name, "n_tokens": n, "heads": h, "head_dim": 128, "batch": 1,
+                   "video_grid": list(wl.grid), "audio_tokens": wl.audio, "text_tokens": wl.text,
+                   "parallelism": "single-gpu"},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels": {"prep_ms": round(prep_ms, 4), "forward_ms": round(fwd_ms, 4),
+                    "prep_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "mfma", "kernel": "h3attn_forward", "achieved": round(fwd_tflops, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(fwd_tflops / peak, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, cfg, inp, args.cpu_rows, args.cpu_heads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

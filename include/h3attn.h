@@ -1,0 +1,199 @@
+/*
+ * h3attn.h - C ABI of the packed joint-attention library for MI355X (gfx950).
+ *
+ * One H3 denoiser block attends over a single packed sequence of video, audio
+ * and text tokens with one softmax per query row and no padding of semantic
+ * tokens ("H3 Blackwell Runtime Plan", Architecture and Non-Negotiable
+ * Validation).  In front of the attention, Q and K get a per-head RMSNorm and
+ * a 3-axis (t, h, w) split-half RoPE ("H3 Runtime Current State", Owned
+ * Performance Kernels: the entry fusion of strided-NHD Q/K RMSNorm, split-half
+ * RoPE and Q quantisation; "H3 Blackwell Runtime Plan", 2026-08-15 Handoff:
+ * fused Q/K RMS + RoPE + HND layout).
+ *
+ * Two calls carry the path:
+ *   h3attn_prep     RMSNorm + RoPE of Q and K, written head-major (HND),
+ *                   either as bf16 or as int8 codes with per-64-token scales.
+ *   h3attn_forward  softmax(Q' K'^T * scale) V, written token-major (NHD).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are DEVICE pointers (memory of the current HIP
+ *   device); the problem descriptor is a HOST pointer.
+ * - The caller owns every buffer.  The library never allocates, never frees,
+ *   never synchronises and keeps no state between calls; calls on different
+ *   streams may run concurrently.  `stream` is a hipStream_t (NULL = the
+ *   default stream).  Work is enqueued on `stream`; results are ready when the
+ *   stream reaches that point.
+ * - Strides are in ELEMENTS of the tensor's type, the last (head-dim) axis is
+ *   contiguous.  Q/K/V inputs are strided NHD views, e.g. slices of an
+ *   interleaved QKV projection output ("H3 Runtime Current State", Owned
+ *   Performance Kernels: Q/K/V stay strided views and the attention emits
+ *   contiguous token-major NHD output).
+ * - Every argument is checked on the host before anything is enqueued; a
+ *   rejected call enqueues nothing and returns a negative h3attn_status.
+ *   There is no fallback path: unsupported input is an error.
+ * - Numbers: bf16 is IEEE binary32 truncated to 16 bits (8-bit exponent);
+ *   rounding to bf16 is to nearest, ties to even.
+ */
+#ifndef H3ATTN_H
+#define H3ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3ATTN_ABI_VERSION 1
+
+typedef enum {
+    H3ATTN_OK = 0,
+    H3ATTN_E_NULL = -1,         /* a required pointer is NULL                         */
+    H3ATTN_E_SHAPE = -2,        /* bad N/H/sections/strides/window/scale value         */
+    H3ATTN_E_UNSUPPORTED = -3,  /* head_dim != 128, unknown format, sections not /16   */
+    H3ATTN_E_ALIGN = -4,        /* pointer not 16-byte aligned or stride not /8 (/16) */
+    H3ATTN_E_ALIAS = -5,        /* an output byte range overlaps another buffer        */
+    H3ATTN_E_HIP = -6           /* the HIP runtime reported an error on launch         */
+} h3attn_status;
+
+/* Storage of the prepped Q'/K' tensors. */
+typedef enum {
+    H3ATTN_QK_BF16 = 0,         /* bf16 values                                          */
+    H3ATTN_QK_I8_BLK64 = 1      /* int8 codes + one fp32 scale per 64 tokens per head   */
+} h3attn_qk_format;
+
+/* Problem descriptor (host memory). */
+typedef struct {
+    int32_t n_tokens;           /* N >= 1: packed video + audio + text tokens           */
+    int32_t n_heads;            /* H >= 1                                               */
+    int32_t head_dim;           /* d: must be 128                                       */
+    int32_t rope_sections[3];   /* widths of the t, h, w slices of d, in this order:
+                                   contiguous [0,s0), [s0,s0+s1), [s0+s1,d); each >= 0,
+                                   a multiple of 16, summing to d (e.g. 32, 48, 48)    */
+    float rope_theta;           /* RoPE base, > 0 (e.g. 10000)                          */
+    float rms_eps;              /* RMSNorm epsilon, >= 0 (e.g. 1e-6)                    */
+    int32_t qk_format;          /* h3attn_qk_format                                     */
+} h3attn_problem;
+
+/* Rows per head of the prepped Q'/K' buffers: N rounded up to a multiple of
+ * 256.  Rows N..N_pad-1 are written by h3attn_prep (zeros) and never form
+ * part of any softmax.  Returns 0 for an invalid descriptor. */
+int64_t h3attn_padded_tokens(const h3attn_problem* p);
+
+/* Bytes of ONE prepped tensor (Q' or K'): H * N_pad * 128 * (2 for bf16,
+ * 1 for int8).  Returns 0 for an invalid descriptor. */
+size_t h3attn_prepped_qk_bytes(const h3attn_problem* p);
+
+/* Bytes of ONE scale array (Q' or K') in int8 format: H * ceil(N/64) * 4,
+ * fp32 [H][ceil(N/64)]; 0 in bf16 format or for an invalid descriptor. */
+size_t h3attn_scales_bytes(const h3attn_problem* p);
+
+/*
+ * h3attn_prep - per-head RMSNorm, then 3-axis split-half RoPE, of Q and K.
+ *
+ * For every token n < N, head h and tensor X in {Q, K}, with x = X[n, h, :]
+ * widened from bf16 to fp32:
+ *   y = x / sqrt(mean_c(x_c^2) + eps) * gamma_X[h, :]
+ * then, for each section a in (t, h, w) at offset o of width s, each j < s/2:
+ *   phi = pos_thw[n][a] * theta^(-2j/s)
+ *   (y[o+j], y[o+j+s/2]) <- (y[o+j] cos phi - y[o+j+s/2] sin phi,
+ *                            y[o+j+s/2] cos phi + y[o+j] sin phi)
+ * ("H3 Runtime Current State", Owned Performance Kernels: Q/K RMSNorm and
+ * split-half RoPE; "H3 Blackwell Runtime Plan", Architecture: 3-axis RoPE).
+ * Arithmetic is fp32; the result is rounded once to bf16.
+ *
+ * bf16 format: q_out/k_out are bf16 [H][N_pad][128] (HND, row stride 128).
+ * int8 format: the bf16-rounded values of each head are grouped in blocks of
+ *   64 tokens from token 0 (the last block may be partial); with a = max|y|
+ *   over the block (fp32), scale = a/127 and inv = 127/a (IEEE fp32 division,
+ *   round to nearest even) and code = clamp(rint(y * inv), -127, 127) (fp32
+ *   product, rint ties-to-even); a == 0 gives scale 0 and zero codes.
+ *   q_out/k_out are int8 [H][N_pad][128]; q_scales/k_scales are fp32
+ *   [H][ceil(N/64)].  This is the int8 Q/K step of the quantised attention
+ *   path ("H3 Runtime Current State", Owned Performance Kernels: Q
+ *   quantization and K quantization), without K-mean smoothing.
+ * Rows n >= N of q_out/k_out are written as zeros in both formats.
+ *
+ * q, k:      bf16 views, element (n,h,c) at base + n*stride_tok + h*stride_head + c;
+ *            16-byte aligned, strides >= 0 and multiples of 8.
+ * gamma_q/k: bf16; element (h,c) at base + h*gamma_head_stride + c;
+ *            gamma_head_stride = 0 shares one [128] vector by all heads;
+ *            16-byte aligned, stride >= 0 and a multiple of 8.
+ * pos_thw:   int32 [N][3] (t, h, w) positions, 4-byte aligned.
+ * q_out/k_out: h3attn_prepped_qk_bytes(p) bytes each, 16-byte aligned.
+ * q_scales/k_scales: h3attn_scales_bytes(p) bytes each (4-byte aligned) in
+ *            int8 format; must be NULL in bf16 format.
+ * Outputs must not overlap each other or any input.
+ * Errors: E_NULL, E_SHAPE, E_UNSUPPORTED, E_ALIGN, E_ALIAS (nothing is
+ * enqueued), E_HIP (launch failure).
+ */
+int h3attn_prep(const h3attn_problem* p,
+                const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                const void* gamma_q, const void* gamma_k, int64_t gamma_head_stride,
+                const int32_t* pos_thw,
+                void* q_out, void* k_out, float* q_scales, float* k_scales,
+                void* stream);
+
+/*
+ * h3attn_forward - non-causal attention over the whole packed sequence.
+ *
+ * For every head h and query n < N:
+ *   O[n, h, :] = sum_m softmax_m(softmax_scale * <Q'[h,n,:], K'[h,m,:]>) V[m, h, :]
+ * over all m < N: one softmax per row, no mask, no padding keys ("H3 Blackwell
+ * Runtime Plan", Architecture: ragged Ulysses runs attention on the full packed
+ * tokens; Non-Negotiable Validation: never pad semantic tokens).
+ * In int8 format the logit is S_int * s_q[h, n/64] * s_k[h, m/64] *
+ * softmax_scale with S_int the exact int32 dot product of the codes.
+ * Accumulation is fp32; the probabilities are rounded to bf16 for the P V
+ * product; the output is rounded once to bf16.
+ *
+ * q_prep/k_prep: the outputs of h3attn_prep for the same descriptor
+ *            (bf16 or int8 [H][N_pad][128]); q_scales/k_scales as written
+ *            by h3attn_prep (int8 format) or NULL (bf16 format).
+ * v:         bf16 view [N][H][128] with strides as for q in h3attn_prep.
+ * o:         bf16 output view; element (n,h,c) at o + n*o_stride_tok +
+ *            h*o_stride_head + c; 16-byte aligned, strides multiples of 8,
+ *            and the view must not overlap itself (either o_stride_head >= 128
+ *            and o_stride_tok >= (H-1)*o_stride_head + 128, or o_stride_tok >=
+ *            128 and o_stride_head >= (N-1)*o_stride_tok + 128).  Only rows
+ *            n < N are written.
+ * softmax_scale: finite and > 0 (e.g. 1/sqrt(128)).
+ * o must not overlap any input.
+ * Errors: as for h3attn_prep.
+ */
+int h3attn_forward(const h3attn_problem* p,
+                   const void* q_prep, const void* k_prep,
+                   const float* q_scales, const float* k_scales,
+                   const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                   void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                   float softmax_scale, void* stream);
+
+/*
+ * h3attn_debug_scores_i32 - test hook for the int8 format: the exact int32
+ * Q'K'^T of one head over a window, computed by the same matrix-core tile
+ * routine that h3attn_forward uses for its logits.
+ *   out[r][c] = sum_d q_codes[head][row0 + r][d] * k_codes[head][col0 + c][d]
+ * for r < nrows, c < ncols (out is int32 [nrows][ncols], row-major, device).
+ * Requires the int8 format, 0 <= head < H, nrows, ncols >= 1,
+ * 0 <= row0, row0 + nrows <= N, 0 <= col0, col0 + ncols <= N.
+ * Errors: as for h3attn_prep.
+ */
+int h3attn_debug_scores_i32(const h3attn_problem* p,
+                            const void* q_codes, const void* k_codes,
+                            int32_t head, int32_t row0, int32_t nrows,
+                            int32_t col0, int32_t ncols,
+                            int32_t* out, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* h3attn_status_string(int status);
+
+/* H3ATTN_ABI_VERSION of the built library. */
+int h3attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3ATTN_H */

@@ -1,0 +1,160 @@
+"""CPU tests of the C ABI: the library loads, exports what the header declares,
+and rejects bad arguments on the host before anything reaches the GPU.
+
+Pointers passed here are fake addresses: every call below is rejected by the
+host-side checks, so nothing is dereferenced and no HIP call is made.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from audio_video_diffusion_amd import h3attn as A
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "h3attn.h")
+
+F = 0x7f0000000000          # fake, 16-byte aligned "device" addresses, far apart
+G = 0x7f1000000000
+H = 0x7f2000000000
+I = 0x7f3000000000
+J = 0x7f4000000000
+K = 0x7f5000000000
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(h3attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"h3attn_prep", "h3attn_forward", "h3attn_debug_scores_i32"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (h3attn_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(A.lib, n)
+
+
+def test_abi_version_and_status_strings():
+    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 1
+    for s in (0, -1, -2, -3, -4, -5, -6, 7):
+        assert A.lib.h3attn_status_string(s)
+
+
+def test_sizes():
+    p = A.problem(129410, 24)
+    assert A.padded_tokens(p) == 129536
+    assert A.prepped_qk_bytes(p) == 24 * 129536 * 128 * 2
+    assert A.scales_bytes(p) == 0
+    p8 = A.problem(246462, 24, A.QK_I8_BLK64)
+    assert A.prepped_qk_bytes(p8) == 24 * 246528 * 128
+    assert A.scales_bytes(p8) == 24 * 3851 * 4
+    assert A.padded_tokens(A.problem(1, 1)) == 256
+    assert A.padded_tokens(A.problem(0, 1)) == 0
+    assert A.prepped_qk_bytes(A.problem(10, 1, head_dim=64)) == 0
+
+
+def prep(p, q=F, qst=384, qsh=128, k=G, kst=384, ksh=128, gq=H, gk=H + 256, gsh=0, pos=I,
+         qo=J, ko=J + (1 << 32), qs=None, ks=None):
+    return A.lib.h3attn_prep(ctypes.byref(p), q, qst, qsh, k, kst, ksh, gq, gk, gsh, pos,
+                             qo, ko, qs, ks, None)
+
+
+def fwd(p, q=F, k=G, qs=None, ks=None, v=H, vst=384, vsh=128, o=I, ost=384, osh=128, scale=0.088):
+    return A.lib.h3attn_forward(ctypes.byref(p), q, k, qs, ks, v, vst, vsh, o, ost, osh, scale, None)
+
+
+@pytest.mark.parametrize("kw,field,val,code", [
+    ({}, "head_dim", 64, -3),
+    ({}, "qk_format", 5, -3),
+    ({}, "n_tokens", 0, -2),
+    ({}, "n_heads", 0, -2),
+])
+def test_problem_validation(kw, field, val, code):
+    p = A.problem(1000, 3)
+    setattr(p, field, val)
+    assert prep(p) == code
+    assert fwd(p) == code
+
+
+def test_section_validation():
+    p = A.problem(1000, 3, sections=(32, 48, 32))
+    assert prep(p) == -2                       # does not sum to 128
+    p = A.problem(1000, 3, sections=(40, 40, 48))
+    assert prep(p) == -3                       # not multiples of 16
+    p = A.problem(1000, 3, sections=(-16, 96, 48))
+    assert prep(p) == -2
+    assert prep(A.problem(1000, 3, theta=0.0)) == -2
+    assert prep(A.problem(1000, 3, eps=-1.0)) == -2
+    assert prep(A.problem(1000, 3, eps=float("nan"))) == -2
+
+
+def test_prep_pointer_and_alignment_checks():
+    p = A.problem(1000, 3)
+    assert prep(p, q=None) == -1
+    assert prep(p, k=None) == -1
+    assert prep(p, gq=None) == -1
+    assert prep(p, pos=None) == -1
+    assert prep(p, qo=None) == -1
+    assert prep(p, q=F + 2) == -4             # not 16-byte aligned
+    assert prep(p, qst=383) == -4             # stride not a multiple of 8
+    assert prep(p, qsh=-128) == -2
+    assert prep(p, gsh=4) == -4
+    assert prep(p, qs=K) == -2                # scales given in bf16 format
+    p8 = A.problem(1000, 3, A.QK_I8_BLK64)
+    assert prep(p8) == -1                     # scales missing in int8 format
+    assert prep(p8, qs=K, ks=K + 4096, qo=J + 3) == -4
+
+
+def test_prep_alias_checks():
+    p = A.problem(1000, 3)
+    assert prep(p, qo=F) == -5                          # output on top of q
+    assert prep(p, ko=J + 1000 * 128) == -5             # k_out overlaps q_out
+    assert prep(p, qo=I - 64) == -5                     # overlaps positions
+    p8 = A.problem(1000, 3, A.QK_I8_BLK64)
+    assert prep(p8, qs=J + 16, ks=K) == -5              # scales inside q_out
+
+
+def test_forward_checks():
+    p = A.problem(1000, 3)
+    assert fwd(p, q=None) == -1
+    assert fwd(p, v=None) == -1
+    assert fwd(p, o=None) == -1
+    assert fwd(p, scale=0.0) == -2
+    assert fwd(p, scale=float("inf")) == -2
+    assert fwd(p, scale=-0.1) == -2
+    assert fwd(p, o=I + 8) == -4
+    assert fwd(p, ost=100) == -4
+    assert fwd(p, ost=128, osh=128) == -2                # output rows overlap each other
+    assert fwd(p, ost=384, osh=64) == -2
+    assert fwd(p, qs=K) == -2                            # scales in bf16 format
+    assert fwd(p, o=F + 4096) == -5                      # output inside q'
+    assert fwd(p, o=H + 384 * 10) == -5                  # output inside v
+    p8 = A.problem(1000, 3, A.QK_I8_BLK64)
+    assert fwd(p8) == -1
+    assert fwd(p8, qs=K, ks=K + 4096, o=K + 16) == -5
+
+
+def test_debug_scores_checks():
+    p8 = A.problem(300, 2, A.QK_I8_BLK64)
+    call = lambda p=p8, head=0, r0=0, nr=10, c0=0, nc=10, out=K: A.lib.h3attn_debug_scores_i32(
+        ctypes.byref(p), F, G, head, r0, nr, c0, nc, out, None)
+    assert call(p=A.problem(300, 2)) == -3
+    assert call(head=2) == -2
+    assert call(head=-1) == -2
+    assert call(nr=0) == -2
+    assert call(r0=295, nr=6) == -2
+    assert call(c0=300) == -2
+    assert call(out=None) == -1
+    assert call(out=F + 64) == -5
+
+
+def test_binding_rejects_non_nhd_views():
+    torch = pytest.importorskip("torch")
+    p = A.problem(4, 1)
+    x = torch.zeros(4, 1, 128, dtype=torch.bfloat16).transpose(1, 2)
+    with pytest.raises(ValueError):
+        A.forward(p, x, x, x, x, 0.1)
