@@ -20,7 +20,7 @@ ARCH = "gfx950"
 # Packed fp32 VALU forms are kept out of the generated code.  No fast-math: the
 # int8 quantiser relies on correctly rounded fp32 division.
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]

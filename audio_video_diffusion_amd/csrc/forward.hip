@@ -390,6 +390,7 @@ __global__ void __launch_bounds__(256) scores_i8_kernel(ScoreParams P) {
 }
 
 hipError_t launch_forward(const FwdParams& P, bool int8, hipStream_t stream) {
+    (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
     dim3 grid(kXcds * P.per_xcd), block(256);
     if (int8)
         hipLaunchKernelGGL(fwd_kernel<true>, grid, block, 0, stream, P);
@@ -399,6 +400,7 @@ hipError_t launch_forward(const FwdParams& P, bool int8, hipStream_t stream) {
 }
 
 hipError_t launch_scores_i8(const ScoreParams& P, hipStream_t stream) {
+    (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
     const int r_lo = (P.row0 / kBM) * kBM, c_lo = (P.col0 / kBN) * kBN;
     const int ry = (P.row0 + P.nrows - r_lo + kBM - 1) / kBM;
     const int cx = (P.col0 + P.ncols - c_lo + kBN - 1) / kBN;

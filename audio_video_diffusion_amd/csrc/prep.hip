@@ -121,12 +121,16 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
     for (int t = 0; t < 2; ++t) {
         tok[t] = t0 + row + 32 * t;
         valid[t] = tok[t] < P.n;
-        const float pv = valid[t] ? (float)P.pos[(int64_t)tok[t] * 3 + sl.axis] : 0.f;
+        // the angle pos * theta^(-2j/s) is formed and reduced in fp64: with positions
+        // in the thousands an fp32 product alone is off by ~1e-4 rad
+        const double pv = valid[t] ? (double)P.pos[(int64_t)tok[t] * 3 + sl.axis] : 0.0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float j = (float)(sl.j0 + i);
-            const float omega = powf(P.theta, -2.0f * j / (float)sl.width);
-            sincosf(pv * omega, &sn[t][i], &cs[t][i]);
+            const double j = (double)(sl.j0 + i);
+            const double phi = pv * pow((double)P.theta, -2.0 * j / (double)sl.width);
+            const double two_pi = 6.283185307179586476925;
+            const float r = (float)(phi - two_pi * rint(phi / two_pi));
+            sincosf(r, &sn[t][i], &cs[t][i]);
         }
     }
 
@@ -235,6 +239,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
 }
 
 hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream) {
+    (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
     dim3 grid(P.npad / 64), block(256);
     if (int8)
         hipLaunchKernelGGL(prep_kernel<true>, grid, block, 0, stream, P);

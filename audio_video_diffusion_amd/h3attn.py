@@ -54,7 +54,20 @@ def problem(n_tokens: int, n_heads: int, qk_format: int = QK_BF16, head_dim: int
     return p
 
 
+def _hip_runtimes():
+    """Distinct HIP runtime files mapped into this process."""
+    try:
+        maps = open("/proc/self/maps").read().splitlines()
+    except OSError:
+        return set()
+    return {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+
+
 def _load():
+    # torch brings its own HIP runtime; it must be the only one in the process,
+    # so it is loaded first and the library's libamdhip64.so.7 dependency
+    # resolves to it (same soname).  Streams and device memory come from torch.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m audio_video_diffusion_amd.build` "
                           "(the HIP library is required; there is no fallback)")
@@ -77,6 +90,8 @@ def _load():
         fn.restype, fn.argtypes = res, args
     if lib.h3attn_abi_version() != ABI_VERSION:
         raise ImportError("libh3attn.so ABI version mismatch: rebuild it")
+    if len(_hip_runtimes()) > 1:
+        raise ImportError(f"more than one HIP runtime is loaded: {sorted(_hip_runtimes())}")
     return lib
 
 

@@ -53,7 +53,11 @@ def test_prep_bf16_matches_oracle(cfg, n, h, per_head):
     for got_t, ref in ((q_out, qp), (k_out, kp)):
         got_all = f64(got_t)
         got = got_all[:, :wl.n_tokens, :].transpose(1, 0, 2)
-        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5), np.max(np.abs(got - ref))
+        # bf16 rounding of an fp32 evaluation: half an ulp (<= 2^-8 |y|) plus an fp32
+        # evaluation error of at most 2^-14 |y| that may tip a near-midpoint rounding
+        err = np.abs(got - ref)
+        bound = 2.0 ** -8 * (1 + 2.0 ** -6) * np.abs(ref) + 4e-6
+        assert np.all(err <= bound), (np.max(err - bound), np.max(err))
         assert np.all(got_all[:, wl.n_tokens:, :] == 0)           # pad rows zeroed
 
 
@@ -95,7 +99,7 @@ def test_forward_bf16_matches_oracle(n):
     v = O.bf16_bits_to_f64(inp.v)
     # attention stage alone: oracle attention on the GPU's own prepped Q'/K'
     ref_stage = O.attention(_hnd_to_nhd(q_out, wl.n_tokens), _hnd_to_nhd(k_out, wl.n_tokens), v, SCALE)
-    check(got, ref_stage, max_abs=1e-2, mean_abs=1e-3, rel_l2=6e-3, what="stage")
+    check(got, ref_stage, max_abs=1e-2, mean_abs=MEAN_ABS, rel_l2=6e-3, what="stage")
     # whole path against the fp64 oracle
     qp, kp = _prep_ref(inp)
     check(got, O.attention(qp, kp, v, SCALE), what="e2e")
@@ -272,10 +276,13 @@ def test_int8_forward_matches_oracle(cfg, n, h):
     qv, kv = f64(q16), f64(k16)
     ref_stage = np.stack([oracle_rows_i8(inp, hh, rows, q_bf16=qv[hh, :wl.n_tokens], k_bf16=kv[hh, :wl.n_tokens])
                           for hh in range(wl.heads)], axis=1)
-    check(got, ref_stage, max_abs=1e-2, mean_abs=1e-3, rel_l2=6e-3, what="int8 stage")
+    check(got, ref_stage, max_abs=1e-2, mean_abs=MEAN_ABS, rel_l2=6e-3, what="int8 stage")
     qp, kp = _prep_ref(inp)
     ref = O.attention(qp, kp, O.bf16_bits_to_f64(inp.v), SCALE)
-    check(got, ref, rel_l2=REL_L2_I8, what="int8 vs fp64")
+    if n is None:       # the tiny workload itself: the absolute bounds of the workload definition
+        check(got, ref, rel_l2=REL_L2_I8, what="int8 vs fp64")
+    else:               # few keys -> O(1) outputs: the int8 step error is gated relatively
+        check(got, ref, max_abs=2 * MAX_ABS, mean_abs=2 * MEAN_ABS, rel_l2=REL_L2_I8, what="int8 vs fp64")
 
 
 def test_int8_full_workload_sampled_rows():
