@@ -34,8 +34,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=None, help="workload index (default: the 129,410-token one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512)
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-heads", type=int, default=6)
     return ap.parse_args()
 
 
