@@ -11,212 +11,243 @@
 // * a work-group owns 256 query rows of one head; each wave owns 64 rows as
 //   two 32-row MFMA blocks and keeps its Q' rows in registers;
 // * the work-group streams K'/V in tiles of 64 keys through double-buffered
-//   LDS: K' as [key][d] rows (permuted, see kperm), V transposed to [d][key];
+//   LDS: K' goes global -> LDS directly (global_load_lds_dwordx4) into
+//   permuted rows with XOR-swizzled 16-byte chunks; V is transposed to
+//   [d][key] on its way through registers;
 // * everything is computed transposed so that one lane owns one query column:
 //     S^T (keys x queries) = K' Q'^T     with v_mfma_f32_32x32x16_bf16
 //                                        (int8: v_mfma_i32_32x32x32_i8)
 //     O^T (d x queries)   += V^T P^T     with v_mfma_f32_32x32x16_bf16
-//   The row max and row sum of a query are then in-lane reductions plus one
+//   The row max and row sum of a query are in-lane reductions plus one
 //   exchange between lane l and l^32, and the rescale of O touches only the
 //   lane's own accumulators;
 // * K' rows are placed in LDS so that the 32x32 accumulator layout of S^T
 //   (lane half h holds rows 8i+4h+j) directly yields, per lane, 8 consecutive
 //   keys for each 16-key step of the P V product: P needs no lane movement;
+// * software pipeline: while the matrix cores compute S of tile j+1, the
+//   vector ALUs exponentiate tile j; the P V product of tile j then runs
+//   beside the row max of tile j+1.  One barrier per tile;
 // * online softmax in base 2 with the scale*log2(e) folded into one FMA; the
 //   running max is only raised when it grows by more than 2^8 (exact: the
 //   stale max cancels between numerator and denominator, P stays <= 256);
 // * the blockIdx -> (head, query tile) map keeps the work-groups that one XCD
 //   runs at a time on adjacent query tiles of one head, so K'/V tiles are
 //   shared through that XCD's L2.
+#include <type_traits>
+#ifndef SG_VALU1
+#define SG_VALU1 9
+#endif
+#ifndef SG_VALU2
+#define SG_VALU2 4
+#endif
+
 #include "common.h"
 #include "params.h"
 
 namespace h3 {
-
 
 constexpr int kBM = 256;            // query rows per work-group
 constexpr int kBN = 64;             // keys per tile
 constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;
 
-// LDS row pitches in bytes (16-byte pad keeps ds_read_b128 row groups conflict free)
+// LDS tile sizes in bytes; three buffers of each are in flight
 template <bool kInt8> struct Lds {
-    static constexpr int kRow = (kInt8 ? 128 : 256) + 16;    // K' row
+    static constexpr int kRow = kInt8 ? 128 : 256;            // K' row, unpadded (swizzled)
     static constexpr int kBytes = kBN * kRow;
-    static constexpr int vRow = kBN * 2 + 16;                 // V^T row (64 keys)
-    static constexpr int vBytes = kHeadDim * vRow;
-    static constexpr int stage = kBytes + vBytes;
+    static constexpr int vRow = kHeadDim * 2;                 // V row [key][d], unpadded (swizzled)
+    static constexpr int vBytes = kBN * vRow;
+    static constexpr int kDmaPerWave = kBytes / 1024 / 4;     // global_load_lds_dwordx4 per wave
+    static constexpr int vDmaPerWave = vBytes / 1024 / 4;
 };
+constexpr int kStages = 3;
 
-// LDS row of key (0..63) of a tile: inverse of the accumulator row order, so
-// that accumulator element 8s+e of lane half h is key 16s + 8h + e of its block.
-__device__ __forceinline__ int kperm(int key) {
-    const int blk = key >> 5, kk = key & 31;
-    const int i = 2 * (kk >> 4) + ((kk >> 2) & 1);
-    const int hh = (kk >> 3) & 1;
-    return 32 * blk + 8 * i + 4 * hh + (kk & 3);
+// Tile-local key held by LDS row rho: the 32x32 accumulator row order
+// (rows 8i + 4h + j) mapped so that accumulator element 8s+e of lane half h
+// is key 16s + 8h + e of its 32-key block.
+__device__ __forceinline__ int key_of_row(int rho) {
+    const int blk = rho >> 5, r = rho & 31;
+    const int i = r >> 3, hh = (r >> 2) & 1, j = r & 3;
+    return 32 * blk + 16 * (i >> 1) + 8 * hh + 4 * (i & 1) + j;
 }
 
-// ---- staging of one K'/V tile: global -> registers -> LDS ------------------
+// One 16-byte-per-lane global -> LDS DMA.  Issued as asm so the compiler does
+// not treat it as an LDS write it must wait for before later LDS reads: the
+// kernel's own vmcnt + barrier protocol orders every buffer's fill before use.
+__device__ __forceinline__ void dma16(const void* src, const uint8_t* lds_dst) {
+    const uint32_t dst = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_dst;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
+}
 
-template <bool kInt8> struct Stage {
-    u32x4 kreg[kInt8 ? 2 : 4];
-    u32x4 vreg[4];
-};
+// ---- K' tile: global -> LDS directly ---------------------------------------
 
+// Slot c of LDS row rho holds 16-byte chunk c ^ (rho mod chunks-per-row) of the
+// row's key: lanes reading one chunk of 8 (16) consecutive rows hit distinct banks.
 template <bool kInt8>
-__device__ __forceinline__ void stage_load(Stage<kInt8>& st, const FwdParams& P, const uint8_t* khead,
-                                           const uint16_t* vhead, int key0, int tid) {
-    constexpr int rowB = kInt8 ? 128 : 256;
+__device__ __forceinline__ void k_tile_async(const uint8_t* khead, int key0, uint8_t* kbuf, int wave,
+                                             int lane) {
+    constexpr int rowB = Lds<kInt8>::kRow;
+    constexpr int cpr = rowB / 16;          // chunks per row: 16 (bf16) or 8 (int8)
+    constexpr int rpi = 64 / cpr;           // rows per wave instruction: 4 or 8
 #pragma unroll
-    for (int r = 0; r < (kInt8 ? 2 : 4); ++r) {
-        const int g = tid + 256 * r;             // 16-byte chunk of the contiguous tile
-        st.kreg[r] = ld16(khead + (int64_t)key0 * rowB + (int64_t)g * 16);
-    }
-    const int kg = tid & 15, dc = tid >> 4;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int key = key0 + 4 * kg + r;
-        st.vreg[r] = key < P.n ? ld16(vhead + (int64_t)key * P.v_st + 8 * dc) : u32x4{0, 0, 0, 0};
+    for (int r = 0; r < 16 / rpi; ++r) {    // each wave fills 16 rows
+        const int row0 = 16 * wave + rpi * r;
+        const int rho = row0 + lane / cpr;
+        const int c = (lane % cpr) ^ (rho & (cpr - 1));
+        const uint8_t* src = khead + (int64_t)(key0 + key_of_row(rho)) * rowB + c * 16;
+        dma16(src, kbuf + row0 * rowB);
     }
 }
 
-template <bool kInt8>
-__device__ __forceinline__ void stage_store(const Stage<kInt8>& st, uint8_t* lds, int tid) {
-    using L = Lds<kInt8>;
-    constexpr int chunks = kInt8 ? 8 : 16;      // 16-byte chunks per K' row
+// ---- V tile: global -> LDS directly, row-major [key][d] ---------------------
+
+// Slot c of V row kappa holds 16-byte chunk c ^ 4(kappa mod 4); rows past N
+// re-read row N-1 (their probabilities are exactly 0).
+__device__ __forceinline__ void v_tile_async(const uint16_t* vhead, int64_t v_st, int key0, int n,
+                                             uint8_t* vbuf, int wave, int lane) {
 #pragma unroll
-    for (int r = 0; r < (kInt8 ? 2 : 4); ++r) {
-        const int g = tid + 256 * r;
-        const int key = g / chunks, ch = g % chunks;
-        *reinterpret_cast<u32x4*>(lds + kperm(key) * L::kRow + ch * 16) = st.kreg[r];
-    }
-    uint8_t* vt = lds + L::kBytes;
-    const int kg = tid & 15, dc = tid >> 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // column pair (2i, 2i+1) of the chunk for keys 4kg..4kg+3
-        const uint32_t a0 = st.vreg[0][i], a1 = st.vreg[1][i], a2 = st.vreg[2][i], a3 = st.vreg[3][i];
-        const u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        const u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        const int d = 8 * dc + 2 * i;
-        *reinterpret_cast<u32x2*>(vt + d * L::vRow + kg * 8) = lo;
-        *reinterpret_cast<u32x2*>(vt + (d + 1) * L::vRow + kg * 8) = hi;
+    for (int r = 0; r < 4; ++r) {                 // each wave fills 16 rows, 4 per instruction
+        const int row0 = 16 * wave + 4 * r;
+        const int kappa = row0 + (lane >> 4);
+        const int c = (lane & 15) ^ (4 * (kappa & 3));
+        const int key = min(key0 + kappa, n - 1);
+        const uint16_t* src = vhead + (int64_t)key * v_st + c * 8;
+        dma16(src, vbuf + row0 * 256);
     }
 }
 
 // ---- S^T = K' Q'^T for one tile: S[kb][qb] is keys 32kb.. x queries 32qb.. --
 
-__device__ __forceinline__ void qk_tile_bf16(const uint8_t* klds, const bf16x8 (&qreg)[2][8],
-                                             f32x16 (&S)[2][2], int n32, int hh) {
-    using L = Lds<false>;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        S[kb][0] = f32x16{};
-        S[kb][1] = f32x16{};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(klds + (32 * kb + n32) * L::kRow + 32 * t + 16 * hh);
-            S[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0][t], S[kb][0], 0, 0, 0);
-            S[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[1][t], S[kb][1], 0, 0, 0);
-        }
-    }
+// S accumulates in arch VGPRs (the softmax reads it with VALU ops) while Q'
+// stays in AGPRs: these MFMAs are issued as inline asm to pin the register
+// classes.  The first of a chain writes an early-clobber destination (it must
+// not overlap the A/B operands); the rest accumulate in place.
+__device__ __forceinline__ void mfma_s(f32x16& d, const bf16x8& a, const bf16x8& b, bool first) {
+    if (first)
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
-__device__ __forceinline__ void qk_tile_i8(const uint8_t* klds, const i32x4 (&qreg)[2][4],
-                                           i32x16 (&S)[2][2], int n32, int hh) {
-    using L = Lds<true>;
+// The compiler does not see the latency of the asm MFMAs above: before a VALU
+// op reads their result, 24 wait states (more than the 8-pass XDL -> VALU
+// requirement) are inserted, ordered after the MFMAs through the operand.
+__device__ __forceinline__ void settle(f32x16 (&S)[2][2]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(S[0][0]), "+v"(S[0][1]), "+v"(S[1][0]), "+v"(S[1][1]));
+}
+__device__ __forceinline__ void settle(i32x16 (&)[2][2]) {}
+
+__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const bf16x8 (&q)[2][8], f32x16 (&S)[2][2],
+                                        int n32, int hh) {
+    // all 16 A operands first (they sit in AGPRs), so LDS latency overlaps
+    bf16x8 a[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int rho = 32 * kb + n32;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int slot = (2 * t + hh) ^ (rho & 15);
+            a[kb][t] = *reinterpret_cast<const bf16x8*>(kbuf + rho * 256 + slot * 16);
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            mfma_s(S[kb][0], a[kb][t], q[0][t], t == 0);
+            mfma_s(S[kb][1], a[kb][t], q[1][t], t == 0);
+        }
+}
+
+__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const i32x4 (&q)[2][4], i32x16 (&S)[2][2],
+                                        int n32, int hh) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         S[kb][0] = i32x16{};
         S[kb][1] = i32x16{};
+        const int rho = 32 * kb + n32;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const i32x4 a = *reinterpret_cast<const i32x4*>(klds + (32 * kb + n32) * L::kRow + 32 * t + 16 * hh);
-            S[kb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[0][t], S[kb][0], 0, 0, 0);
-            S[kb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qreg[1][t], S[kb][1], 0, 0, 0);
+            const int slot = (2 * t + hh) ^ (rho & 7);
+            const i32x4 a = *reinterpret_cast<const i32x4*>(kbuf + rho * 128 + slot * 16);
+            S[kb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, q[0][t], S[kb][0], 0, 0, 0);
+            S[kb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, q[1][t], S[kb][1], 0, 0, 0);
         }
     }
 }
 
 // Q' rows of one wave as MFMA B operands: lane (n32, hh) holds row q0+32qb+n32.
-__device__ __forceinline__ void load_q_bf16(const uint8_t* qhead, int q0, int n32, int hh, bf16x8 (&qreg)[2][8]) {
+__device__ __forceinline__ void load_q(const uint8_t* qhead, int q0, int n32, int hh, bf16x8 (&q)[2][8]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-            qreg[qb][t] = __builtin_bit_cast(bf16x8, ld16(qhead + (int64_t)(q0 + 32 * qb + n32) * 256 + 32 * t + 16 * hh));
+            q[qb][t] = __builtin_bit_cast(bf16x8, ld16(qhead + (int64_t)(q0 + 32 * qb + n32) * 256 + 32 * t + 16 * hh));
 }
 
-__device__ __forceinline__ void load_q_i8(const uint8_t* qhead, int q0, int n32, int hh, i32x4 (&qreg)[2][4]) {
+__device__ __forceinline__ void load_q(const uint8_t* qhead, int q0, int n32, int hh, i32x4 (&q)[2][4]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            qreg[qb][t] = __builtin_bit_cast(i32x4, ld16(qhead + (int64_t)(q0 + 32 * qb + n32) * 128 + 32 * t + 16 * hh));
+            q[qb][t] = __builtin_bit_cast(i32x4, ld16(qhead + (int64_t)(q0 + 32 * qb + n32) * 128 + 32 * t + 16 * hh));
 }
 
-// acc *= alpha with acc pinned to the accumulation registers (AGPRs): the rare
-// rescale of the running output then never forces O into arch VGPRs.
-__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
-    float tmp;
+// ---- softmax pieces ---------------------------------------------------------
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(int x) { return (float)x; }
+__device__ __forceinline__ float neg_inf_of(float) { return -INFINITY; }
+__device__ __forceinline__ int neg_inf_of(int) { return INT32_MIN; }
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_fmaxf(a, b); }
+__device__ __forceinline__ int vmax(int a, int b) { return a > b ? a : b; }
+
+// Tile-local key of accumulator element e of block kb for lane half hh.
+__device__ __forceinline__ int key_of_elem(int kb, int e, int hh) {
+    return 32 * kb + 16 * (e >> 3) + 8 * hh + (e & 7);
+}
+
+template <typename V>
+__device__ __forceinline__ void mask_tile(V (&S)[2][2], int key0, int n, int hh) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        float x = acc[e];
-        asm volatile("v_accvgpr_read_b32 %1, %0\n\t"
-                     "v_mul_f32 %1, %1, %2\n\t"
-                     "v_accvgpr_write_b32 %0, %1"
-                     : "+a"(x), "=&v"(tmp) : "v"(alpha));
-        acc[e] = x;
-    }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (key0 + key_of_elem(kb, e, hh) >= n) S[kb][qb][e] = neg_inf_of(S[kb][qb][e]);
 }
 
-// ---- online softmax + P V of one tile --------------------------------------
+// Scaled (base-2) row max of query block qb over the whole tile (both lane halves).
+template <typename V>
+__device__ __forceinline__ float row_max(const V (&S)[2][2], int qb, float coef) {
+    auto mx = S[0][qb][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = vmax(mx, S[kb][qb][e]);
+    float f = to_f(mx) * coef;
+    return fmaxf(f, __shfl_xor(f, 32));
+}
 
-template <bool kMask>
-__device__ __forceinline__ void softmax_pv(f32x16 (&S)[2][2], float coef, const uint8_t* vt,
-                                           f32x16 (&O)[2][4], float (&m)[2], float (&l)[2],
-                                           int key0, int n, int n32, int hh) {
-    using L = Lds<false>;
-    bf16x8 Pb[2][2][2];      // [qb][kb][s]
+// P = exp2(S * coef - m) rounded to bf16 as the P V operands; l += row sums.
+template <bool kMask, typename V>
+__device__ __forceinline__ void exp_tile(const V (&S)[2][2], float coef, const float (&m)[2],
+                                         bf16x8 (&Pb)[2][2][2], float (&l)[2], int key0, int n, int hh) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        if constexpr (kMask) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = key0 + 32 * kb + 16 * (e >> 3) + 8 * hh + (e & 7);
-                    if (key >= n) S[kb][qb][e] = -INFINITY;
-                }
-        }
-        float mx = S[0][qb][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, S[kb][qb][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = mx * coef;
-        if (__any(mnew > m[qb] + kRescaleLog2)) {
-            const float mm = fmaxf(m[qb], mnew);
-            const float alpha = __builtin_amdgcn_exp2f(m[qb] - mm);
-            m[qb] = mm;
-            l[qb] *= alpha;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) scale_acc(O[qb][c], alpha);
-        }
-        const float mq = m[qb];
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             float p[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][qb][e], coef, -mq));
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(to_f(S[kb][qb][e]), coef, -m[qb]));
                 if constexpr (kMask) {
                     // keys >= N: probability exactly 0 (also when coef == 0)
-                    const int key = key0 + 32 * kb + 16 * (e >> 3) + 8 * hh + (e & 7);
-                    if (key >= n) p[e] = 0.f;
+                    if (key0 + key_of_elem(kb, e, hh) >= n) p[e] = 0.f;
                 }
                 rs += p[e];
             }
@@ -230,116 +261,205 @@ __device__ __forceinline__ void softmax_pv(f32x16 (&S)[2][2], float coef, const 
         }
         l[qb] += rs;
     }
+}
+
+// O^T += V^T P^T for one tile.  The A operand (8 consecutive keys of one d
+// column) comes from the row-major V tile through ds_read_b64_tr_b16: in each
+// 16-lane group, output lane i, slot k is element i%4 of the 4 read by lane
+// 4k + i/4, so lane r reads row (key base + r/4), columns D0 + 4(r%4)..+3.
+__device__ __forceinline__ void pv_tile(const uint8_t* vbuf, const bf16x8 (&Pb)[2][2][2], f32x16 (&O)[2][4],
+                                        int lane) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    const int r = lane & 15, g = lane >> 4;
+    const int hhl = g >> 1, dh = g & 1, rk = r >> 2;
+    // byte offset of this lane inside a 4-row group, without the column block c
+    const int lane_off = (8 * hhl + rk) * 256 + (2 * dh + ((r & 3) >> 1)) * 16 + 8 * (r & 1);
+    bf16x8 a[4][2][2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int off_c = lane_off + 64 * (c ^ rk);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int off = off_c + (32 * kb + 16 * s) * 256;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4*)(vbuf + off));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4*)(vbuf + off + 4 * 256));
+                a[c][kb][s] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * c + n32) * L::vRow + 2 * (32 * kb + 16 * s + 8 * hh));
-                O[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Pb[0][kb][s], O[0][c], 0, 0, 0);
-                O[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Pb[1][kb][s], O[1][c], 0, 0, 0);
+                O[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][kb][s], Pb[0][kb][s], O[0][c], 0, 0, 0);
+                O[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][kb][s], Pb[1][kb][s], O[1][c], 0, 0, 0);
             }
 }
 
-__device__ __forceinline__ void s_to_float(const i32x16 (&Si)[2][2], f32x16 (&S)[2][2]) {
+// acc *= alpha with acc pinned to the accumulation registers (AGPRs): the rare
+// rescale of the running output then never forces O into arch VGPRs.
+__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
+    float tmp;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int e = 0; e < 16; ++e) {
+        float x = acc[e];
+        if (e == 0)      // wait states after the matrix core last wrote acc
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+                         "v_accvgpr_read_b32 %1, %0\n\t"
+                         "v_mul_f32 %1, %1, %2\n\t"
+                         "v_accvgpr_write_b32 %0, %1"
+                         : "+a"(x), "=&v"(tmp) : "v"(alpha));
+        else
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\t"
+                         "v_mul_f32 %1, %1, %2\n\t"
+                         "v_accvgpr_write_b32 %0, %1"
+                         : "+a"(x), "=&v"(tmp) : "v"(alpha));
+        acc[e] = x;
+    }
+}
+
+// Raise the running max when a row's new max exceeds it by more than 2^8.
+__device__ __forceinline__ void maybe_rescale(const float (&mx)[2], float (&m)[2], float (&l)[2],
+                                              f32x16 (&O)[2][4]) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2; ++qb) {
+        if (__any(mx[qb] > m[qb] + kRescaleLog2)) {
+            const float mm = fmaxf(m[qb], mx[qb]);
+            const float alpha = __builtin_amdgcn_exp2f(m[qb] - mm);
+            m[qb] = mm;
+            l[qb] *= alpha;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) S[kb][qb][e] = (float)Si[kb][qb][e];
+            for (int c = 0; c < 4; ++c) scale_acc(O[qb][c], alpha);
+        }
+    }
+}
+
+// Empty asm statements that fix a value's register class at this point: Q' (an
+// MFMA operand only) lives in AGPRs, S (read by the softmax VALU ops) in VGPRs.
+template <typename T, int A, int B>
+__device__ __forceinline__ void pin_agpr(T (&x)[A][B]) {
+#pragma unroll
+    for (int a = 0; a < A; ++a)
+#pragma unroll
+        for (int b = 0; b < B; ++b) asm volatile("" : "+a"(x[a][b]));
+}
+template <typename T, int A, int B>
+__device__ __forceinline__ void pin_vgpr(T (&x)[A][B]) {
+#pragma unroll
+    for (int a = 0; a < A; ++a)
+#pragma unroll
+        for (int b = 0; b < B; ++b) asm volatile("" : "+v"(x[a][b]));
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most the DMA of the current step is outstanding (vmcnt counts
+// in issue order), i.e. the tiles fetched one step earlier have landed.
+template <int kOutstanding>
+__device__ __forceinline__ void wait_vmem_upto() {
+    if constexpr (kOutstanding == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if constexpr (kOutstanding == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <bool kInt8>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 fwd_kernel(FwdParams P) {
     using L = Lds<kInt8>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::stage];
+    using QReg = typename std::conditional<kInt8, i32x4[2][4], bf16x8[2][8]>::type;
+    using SVec = typename std::conditional<kInt8, i32x16, f32x16>::type;
+    constexpr int kDma = L::kDmaPerWave + L::vDmaPerWave;      // per wave per tile
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * (L::kBytes + L::vBytes)];
 
     const int vb = (blockIdx.x % kXcds) * P.per_xcd + blockIdx.x / kXcds;
     if (vb >= P.total) return;                     // whole work-group, before any barrier
     const int head = vb / P.qtiles;
     const int qt = vb % P.qtiles;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n32 = lane & 31, hh = lane >> 5;
     const int q0 = qt * kBM + wave * 64;
+    const int n = P.n;
 
     constexpr int elt = kInt8 ? 1 : 2;
     const uint8_t* qhead = static_cast<const uint8_t*>(P.q) + (int64_t)head * P.npad * kHeadDim * elt;
     const uint8_t* khead = static_cast<const uint8_t*>(P.k) + (int64_t)head * P.npad * kHeadDim * elt;
     const uint16_t* vhead = P.v + (int64_t)head * P.v_sh;
+    const float* kscale = kInt8 ? P.ks + (int64_t)head * P.nblk : nullptr;
+    auto kbuf = [&](int j) { return lds + (j % kStages) * L::kBytes; };
+    auto vbuf = [&](int j) { return lds + kStages * L::kBytes + (j % kStages) * L::vBytes; };
 
-    bf16x8 qb16[2][8];
-    i32x4 qi8[2][4];
-    float qscale = 0.f;
-    if constexpr (kInt8) {
-        load_q_i8(qhead, q0, n32, hh, qi8);
-        qscale = q0 < P.n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
-    } else {
-        load_q_bf16(qhead, q0, n32, hh, qb16);
-    }
+    QReg q;
+    load_q(qhead, q0, n32, hh, q);
+    pin_agpr(q);
+    float qscale = 1.f;
+    if constexpr (kInt8) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
+    auto coef_of = [&](int j) -> float {
+        if constexpr (kInt8) return P.c * qscale * kscale[j];
+        else return P.c;
+    };
 
     f32x16 O[2][4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int c = 0; c < 4; ++c) O[qb][c] = f32x16{};
-    float m[2] = {-INFINITY, -INFINITY};
-    float l[2] = {0.f, 0.f};
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-    const int ntiles = (P.n + kBN - 1) / kBN;
-    const bool ragged = (P.n % kBN) != 0;
-
-    Stage<kInt8> st;
-    stage_load<kInt8>(st, P, khead, vhead, 0, tid);
-    stage_store<kInt8>(st, lds, tid);
-    __syncthreads();
-
-    // S^T of one tile (bf16 or dequantised int8) and its logit coefficient
-    auto scores = [&](const uint8_t* cur, int kt, f32x16 (&S)[2][2]) -> float {
-        if constexpr (kInt8) {
-            i32x16 Si[2][2];
-            qk_tile_i8(cur, qi8, Si, n32, hh);
-            s_to_float(Si, S);
-            return P.c * qscale * P.ks[(int64_t)head * P.nblk + kt];
-        } else {
-            qk_tile_bf16(cur, qb16, S, n32, hh);
-            return P.c;
-        }
+    const int ntiles = (n + kBN - 1) / kBN;
+    const int last = ntiles - 1;
+    const bool ragged = (n % kBN) != 0;
+    // K'_t and V_t land in stage t % 3, fetched two tiles ahead.  Indices past the
+    // last tile re-fetch the last tile into a stage nobody reads any more, so
+    // every tile issues the same number of DMA instructions.
+    auto fetch = [&](int t) {
+        k_tile_async<kInt8>(khead, min(t, last) * kBN, kbuf(t), wave, lane);
+        v_tile_async(vhead, P.v_st, min(t, last) * kBN, n, vbuf(t), wave, lane);
     };
 
-    // all full tiles but the last: no key mask; the next tile is prefetched
-    for (int kt = 0; kt + 1 < ntiles; ++kt) {
-        uint8_t* cur = lds + (kt & 1) * L::stage;
-        stage_load<kInt8>(st, P, khead, vhead, (kt + 1) * kBN, tid);
-        f32x16 S[2][2];
-        const float coef = scores(cur, kt, S);
-        softmax_pv<false>(S, coef, cur + L::kBytes, O, m, l, kt * kBN, P.n, n32, hh);
-        stage_store<kInt8>(st, lds + ((kt + 1) & 1) * L::stage, tid);
-        __syncthreads();
-    }
-    // last tile: keys >= N are masked when N is not a multiple of the tile
-    {
-        const int kt = ntiles - 1;
-        uint8_t* cur = lds + (kt & 1) * L::stage;
-        f32x16 S[2][2];
-        const float coef = scores(cur, kt, S);
-        if (ragged)
-            softmax_pv<true>(S, coef, cur + L::kBytes, O, m, l, kt * kBN, P.n, n32, hh);
+    // One tile: S = K' Q'^T, online softmax, O += P V.
+    auto tile = [&](int j, bool masked) {
+        fetch(j + 2);
+        SVec S[2][2];
+        qk_tile(kbuf(j), q, S, n32, hh);
+        settle(S);
+        if (masked) mask_tile(S, j * kBN, n, hh);
+        const float coef = coef_of(j);
+        float mx[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) mx[qb] = row_max(S, qb, coef);
+        maybe_rescale(mx, m, l, O);
+        bf16x8 Pb[2][2][2];
+        if (masked)
+            exp_tile<true>(S, coef, m, Pb, l, j * kBN, n, hh);
         else
-            softmax_pv<false>(S, coef, cur + L::kBytes, O, m, l, kt * kBN, P.n, n32, hh);
-    }
+            exp_tile<false>(S, coef, m, Pb, l, j * kBN, n, hh);
+        pv_tile(vbuf(j), Pb, O, lane);
+        wait_vmem_upto<kDma>();                    // tile j+1 has landed
+        __syncthreads();
+    };
+
+    fetch(0);
+    fetch(1);
+    wait_vmem_upto<kDma>();
+    __syncthreads();
+    for (int j = 0; j < last; ++j) tile(j, false);
+    tile(last, ragged);
+    wait_vmem_all();                               // no DMA may land after the work-group ends
 
     // epilogue: O^T / l -> bf16, lane (n32, hh) holds d = 32c + 8i + 4hh + j of its query
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const float lt = l[qb] + __shfl_xor(l[qb], 32);
         const float inv = 1.0f / lt;
-        const int q = q0 + 32 * qb + n32;
-        if (q < P.n) {
-            uint16_t* orow = P.o + (int64_t)q * P.o_st + (int64_t)head * P.o_sh;
+        const int qrow = q0 + 32 * qb + n32;
+        if (qrow < n) {
+            uint16_t* orow = P.o + (int64_t)qrow * P.o_st + (int64_t)head * P.o_sh;
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -352,8 +472,7 @@ fwd_kernel(FwdParams P) {
     }
 }
 
-// ---- exact int32 scores of the int8 path (test hook), same tile routine -----
-
+// ---- exact int32 scores of the int8 path (test hook), same tile routines ----
 
 __global__ void __launch_bounds__(256) scores_i8_kernel(ScoreParams P) {
     using L = Lds<true>;
@@ -364,26 +483,22 @@ __global__ void __launch_bounds__(256) scores_i8_kernel(ScoreParams P) {
     const int kbase = (P.col0 / kBN) * kBN + blockIdx.x * kBN;
     const int q0 = qbase + wave * 64;
 
-    i32x4 qreg[2][4];
-    load_q_i8(P.qhead, q0, n32, hh, qreg);
-    for (int r = 0; r < 2; ++r) {                    // same placement as the forward staging
-        const int g = tid + 256 * r;
-        const int key = g / 8, ch = g % 8;
-        *reinterpret_cast<u32x4*>(lds + kperm(key) * L::kRow + ch * 16) =
-            ld16(P.khead + (int64_t)(kbase + key) * 128 + ch * 16);
-    }
+    i32x4 q[2][4];
+    load_q(P.qhead, q0, n32, hh, q);
+    k_tile_async<true>(P.khead, kbase, lds, wave, lane);
+    wait_vmem_all();
     __syncthreads();
     i32x16 S[2][2];
-    qk_tile_i8(lds, qreg, S, n32, hh);
+    qk_tile(lds, q, S, n32, hh);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int q = q0 + 32 * qb + n32;
-                const int key = kbase + 32 * kb + 16 * (e >> 3) + 8 * hh + (e & 7);
-                const int r = q - P.row0, c = key - P.col0;
+                const int qrow = q0 + 32 * qb + n32;
+                const int key = kbase + key_of_elem(kb, e, hh);
+                const int r = qrow - P.row0, c = key - P.col0;
                 if (r >= 0 && r < P.nrows && c >= 0 && c < P.ncols)
                     P.out[(int64_t)r * P.ncols + c] = S[kb][qb][e];
             }
