@@ -26,6 +26,37 @@ PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
 PEAK_INT8_TOPS = 5033.2
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes per h3attn_forward launch on the 1344x768/124-frame bf16 workload,
+# from two rocprofv3 --pmc passes over one bench step (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch).  Each is scaled by what the same counter
+# reports for a plain 1 GiB device copy (bench.py --copy-probe 1024): FETCH_SIZE
+# reads 524,309 KiB there (factor 2.0), WRITE_SIZE 1,048,576 KiB (factor 1.0).
+# The figure belongs to the kernel source it was taken on: when
+# csrc/forward.hip no longer hashes to `source_sha256`, traffic is null.
+FORWARD_TRAFFIC = {
+    "workload": "1344x768_124f",
+    "source_sha256": "f45986932c4732b3ac44f9f18dc2df898538056f49f40983e657193b5321da69",
+    "fetch_kib": 21997586.0, "fetch_scale": 2.0,
+    "write_kib": 776597.8, "write_scale": 1.0,
+}
+
+
+def forward_traffic(workload_name):
+    """Counter-measured HBM bytes per forward launch, or None if stale/other workload."""
+    import hashlib
+    t = FORWARD_TRAFFIC
+    if workload_name != t["workload"]:
+        return None
+    path = os.path.join(ROOT, "audio_video_diffusion_amd", "csrc", "forward.hip")
+    try:
+        with open(path, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if digest != t["source_sha256"]:
+        return None
+    return int(round((t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -36,7 +67,25 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--cpu-heads", type=int, default=6)
+    ap.add_argument("--copy-probe", type=int, default=None, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (counter calibration) and exit")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    """Read MIB MiB and write MIB MiB with one elementwise kernel per call.
+
+    Hardware byte counters (FETCH_SIZE / WRITE_SIZE) read over this run give
+    the factor between what they report and bytes actually moved."""
+    import torch
+    n = mib * (1 << 20) // 2
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 2, "copy_probe_bytes_written": n * 2, "calls": 3}), flush=True)
 
 
 def cpu_baseline(wl, cfg, inp, rows_n, heads_n):
@@ -81,6 +130,10 @@ def main():
               "multi-GPU mode; heads would shard across GPUs with an all-to-all, which is not built.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe is not None:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
     from audio_video_diffusion_amd import h3attn as A
@@ -161,7 +214,8 @@ def main():
                     "prep_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "kernel": "h3attn_forward", "achieved": round(fwd_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(fwd_tflops / peak, 4),
-                     "traffic": None},
+                     "traffic": forward_traffic(wl.name),
+                     "algorithmic_bytes": 4 * n * h * 128 * 2},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
