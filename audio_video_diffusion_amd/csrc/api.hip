@@ -13,6 +13,8 @@
 namespace {
 
 constexpr int64_t kMaxTokens = (int64_t)1 << 30;   // keeps every int32 index in range
+// The forward addresses the 64 V rows of a tile with 32-bit byte offsets.
+constexpr int64_t kMaxVStrideTok = (int64_t)1 << 24;
 
 struct Range {
     uintptr_t lo, hi;    // [lo, hi)
@@ -167,6 +169,7 @@ int h3attn_forward(const h3attn_problem* p,
     if (!i8 && (q_scales || k_scales)) return H3ATTN_E_SHAPE;
     if (i8 && (!aligned(q_scales, 4) || !aligned(k_scales, 4))) return H3ATTN_E_ALIGN;
     if ((rc = check_in_view(v, v_stride_tok, v_stride_head))) return rc;
+    if (v_stride_tok > kMaxVStrideTok) return H3ATTN_E_UNSUPPORTED;
     if ((rc = check_in_view(o, o_stride_tok, o_stride_head))) return rc;
     if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return H3ATTN_E_SHAPE;
 

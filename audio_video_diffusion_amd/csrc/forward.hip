@@ -10,36 +10,32 @@
 // Work decomposition (one 256-thread work-group = 4 wave64s, one per SIMD):
 // * a work-group owns 256 query rows of one head; each wave owns 64 rows as
 //   two 32-row MFMA blocks and keeps its Q' rows in registers;
-// * the work-group streams K'/V in tiles of 64 keys through double-buffered
-//   LDS: K' goes global -> LDS directly (global_load_lds_dwordx4) into
-//   permuted rows with XOR-swizzled 16-byte chunks; V is transposed to
-//   [d][key] on its way through registers;
+// * the work-group streams K'/V in tiles of 64 keys through four LDS stages,
+//   fetched three tiles ahead with buffer -> LDS DMA (buffer_load_dwordx4 ...
+//   lds: 1 KB per wave instruction, no registers in between).  K' rows land
+//   permuted, V rows stay row-major; 16-byte chunks are XOR-swizzled so the
+//   operand reads below hit every LDS bank.  One barrier per tile;
 // * everything is computed transposed so that one lane owns one query column:
 //     S^T (keys x queries) = K' Q'^T     with v_mfma_f32_32x32x16_bf16
 //                                        (int8: v_mfma_i32_32x32x32_i8)
 //     O^T (d x queries)   += V^T P^T     with v_mfma_f32_32x32x16_bf16
 //   The row max and row sum of a query are in-lane reductions plus one
 //   exchange between lane l and l^32, and the rescale of O touches only the
-//   lane's own accumulators;
+//   lane's own accumulators.  V^T operands are read from the row-major V
+//   tile with ds_read_b64_tr_b16, which transposes as it reads;
 // * K' rows are placed in LDS so that the 32x32 accumulator layout of S^T
 //   (lane half h holds rows 8i+4h+j) directly yields, per lane, 8 consecutive
 //   keys for each 16-key step of the P V product: P needs no lane movement;
-// * software pipeline: while the matrix cores compute S of tile j+1, the
-//   vector ALUs exponentiate tile j; the P V product of tile j then runs
-//   beside the row max of tile j+1.  One barrier per tile;
-// * online softmax in base 2 with the scale*log2(e) folded into one FMA; the
-//   running max is only raised when it grows by more than 2^8 (exact: the
-//   stale max cancels between numerator and denominator, P stays <= 256);
+// * online softmax in base 2: one fp32 FMA per score applies scale*log2(e)
+//   (times s_q*s_k in int8 mode) and subtracts the running max m, then exp2.
+//   The running max is only raised when it grows by more than 2^8 (exact: the
+//   stale max cancels between numerator and denominator, P stays <= 256).  The
+//   row sum adds the bf16-rounded P that the P V product uses, two at a time
+//   with a bf16 dot product;
 // * the blockIdx -> (head, query tile) map keeps the work-groups that one XCD
 //   runs at a time on adjacent query tiles of one head, so K'/V tiles are
 //   shared through that XCD's L2.
 #include <type_traits>
-#ifndef SG_VALU1
-#define SG_VALU1 9
-#endif
-#ifndef SG_VALU2
-#define SG_VALU2 4
-#endif
 
 #include "common.h"
 #include "params.h"
@@ -51,7 +47,7 @@ constexpr int kBN = 64;             // keys per tile
 constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;
 
-// LDS tile sizes in bytes; three buffers of each are in flight
+// LDS tile sizes in bytes; four stages of each are in flight
 template <bool kInt8> struct Lds {
     static constexpr int kRow = kInt8 ? 128 : 256;            // K' row, unpadded (swizzled)
     static constexpr int kBytes = kBN * kRow;
@@ -60,7 +56,7 @@ template <bool kInt8> struct Lds {
     static constexpr int kDmaPerWave = kBytes / 1024 / 4;     // global_load_lds_dwordx4 per wave
     static constexpr int vDmaPerWave = vBytes / 1024 / 4;
 };
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 
 // Tile-local key held by LDS row rho: the 32x32 accumulator row order
 // (rows 8i + 4h + j) mapped so that accumulator element 8s+e of lane half h
@@ -80,6 +76,58 @@ __device__ __forceinline__ void dma16(const void* src, const uint8_t* lds_dst) {
                  :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
 }
 
+// Raw buffer resource for `base` (stride 0, no range limit in practice: every
+// offset the kernel forms is inside the tensor).  Word 3 selects the 32-bit
+// data format that gfx9 buffer loads need.
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    r[2] = 0xFFFFFFFFu;
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// One 16-byte-per-lane buffer -> LDS DMA: lane i's 16 bytes at rsrc + voff land
+// at lds_dst + 16 i.  The per-lane offsets stay in registers for the whole
+// kernel; only the scalar base moves from tile to tile.
+__device__ __forceinline__ void dma16_buf(const u32x4& rsrc, uint32_t voff, const uint8_t* lds_dst) {
+    const uint32_t dst = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_dst;
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
+}
+
+// Per-lane byte offsets of one wave's share of a K' tile and of a V tile.
+// K': slot c of LDS row rho holds 16-byte chunk c ^ (rho mod chunks-per-row)
+// of key key_of_row(rho).  V: slot c of row kappa holds chunk c ^ 4(kappa mod
+// 4).  vlast clamps V rows past N to row N-1 for the last tile (first key
+// last_key0): their probabilities are exactly 0, any finite value will do.
+template <bool kInt8>
+struct DmaOffsets {
+    static constexpr int rowB = Lds<kInt8>::kRow;
+    static constexpr int cpr = rowB / 16;
+    static constexpr int rpi = 64 / cpr;
+    static constexpr int kn = 16 / rpi;
+    uint32_t k[kn], v[4], vlast[4];
+    __device__ __forceinline__ DmaOffsets(int wave, int lane, int64_t v_st, int last_key0, int n) {
+#pragma unroll
+        for (int r = 0; r < kn; ++r) {
+            const int rho = 16 * wave + rpi * r + lane / cpr;
+            const int c = (lane % cpr) ^ (rho & (cpr - 1));
+            k[r] = (uint32_t)(key_of_row(rho) * rowB + c * 16);
+        }
+        const uint32_t rs = (uint32_t)(v_st * 2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int kappa = 16 * wave + 4 * r + (lane >> 4);
+            const int c = (lane & 15) ^ (4 * (kappa & 3));
+            v[r] = (uint32_t)kappa * rs + c * 16;
+            vlast[r] = (uint32_t)min(kappa, n - 1 - last_key0) * rs + c * 16;
+        }
+    }
+};
+
 // ---- K' tile: global -> LDS directly ---------------------------------------
 
 // Slot c of LDS row rho holds 16-byte chunk c ^ (rho mod chunks-per-row) of the
@@ -97,23 +145,6 @@ __device__ __forceinline__ void k_tile_async(const uint8_t* khead, int key0, uin
         const int c = (lane % cpr) ^ (rho & (cpr - 1));
         const uint8_t* src = khead + (int64_t)(key0 + key_of_row(rho)) * rowB + c * 16;
         dma16(src, kbuf + row0 * rowB);
-    }
-}
-
-// ---- V tile: global -> LDS directly, row-major [key][d] ---------------------
-
-// Slot c of V row kappa holds 16-byte chunk c ^ 4(kappa mod 4); rows past N
-// re-read row N-1 (their probabilities are exactly 0).
-__device__ __forceinline__ void v_tile_async(const uint16_t* vhead, int64_t v_st, int key0, int n,
-                                             uint8_t* vbuf, int wave, int lane) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {                 // each wave fills 16 rows, 4 per instruction
-        const int row0 = 16 * wave + 4 * r;
-        const int kappa = row0 + (lane >> 4);
-        const int c = (lane & 15) ^ (4 * (kappa & 3));
-        const int key = min(key0 + kappa, n - 1);
-        const uint16_t* src = vhead + (int64_t)key * v_st + c * 8;
-        dma16(src, vbuf + row0 * 256);
     }
 }
 
@@ -232,13 +263,16 @@ __device__ __forceinline__ float row_max(const V (&S)[2][2], int qb, float coef)
     return fmaxf(f, __shfl_xor(f, 32));
 }
 
-// P = exp2(S * coef - m) rounded to bf16 as the P V operands; l += row sums.
+// P = exp2(S * coef - m) rounded to bf16 as the P V operands; l += row sums of
+// those bf16 values (two at a time: a bf16 dot product against (1, 1)).
 template <bool kMask, typename V>
 __device__ __forceinline__ void exp_tile(const V (&S)[2][2], float coef, const float (&m)[2],
                                          bf16x8 (&Pb)[2][2][2], float (&l)[2], int key0, int n, int hh) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        float rs = 0.f;
+        float rs[2] = {0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             float p[16];
@@ -249,17 +283,24 @@ __device__ __forceinline__ void exp_tile(const V (&S)[2][2], float coef, const f
                     // keys >= N: probability exactly 0 (also when coef == 0)
                     if (key0 + key_of_elem(kb, e, hh) >= n) p[e] = 0.f;
                 }
-                rs += p[e];
             }
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
+                // Each pair goes through a bf16x2 value of its own: a bit_cast of
+                // a u32x4 element to bf16x2 feeding the dot product was
+                // miscompiled (every dot read element 0).
                 u32x4 w;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(p[8 * s + 2 * i], p[8 * s + 2 * i + 1]);
+                for (int i = 0; i < 4; ++i) {
+                    const f32x2 f = {p[8 * s + 2 * i], p[8 * s + 2 * i + 1]};
+                    const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+                    rs[s] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs[s], false);
+                    w[i] = __builtin_bit_cast(uint32_t, b);
+                }
                 Pb[qb][kb][s] = __builtin_bit_cast(bf16x8, w);
             }
         }
-        l[qb] += rs;
+        l[qb] += rs[0] + rs[1];
     }
 }
 
@@ -357,11 +398,14 @@ __device__ __forceinline__ void pin_vgpr(T (&x)[A][B]) {
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Wait until at most the DMA of the current step is outstanding (vmcnt counts
-// in issue order), i.e. the tiles fetched one step earlier have landed.
+// Wait until at most kOutstanding of this wave's DMA instructions are still in
+// flight (vmcnt retires in issue order): with the two newest fetches allowed
+// outstanding, every older tile has landed.
 template <int kOutstanding>
 __device__ __forceinline__ void wait_vmem_upto() {
-    if constexpr (kOutstanding == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if constexpr (kOutstanding == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if constexpr (kOutstanding == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if constexpr (kOutstanding == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else if constexpr (kOutstanding == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -414,17 +458,25 @@ fwd_kernel(FwdParams P) {
     const int ntiles = (n + kBN - 1) / kBN;
     const int last = ntiles - 1;
     const bool ragged = (n % kBN) != 0;
-    // K'_t and V_t land in stage t % 3, fetched two tiles ahead.  Indices past the
+    // K'_t and V_t land in stage t % 4, fetched three tiles ahead.  Indices past the
     // last tile re-fetch the last tile into a stage nobody reads any more, so
     // every tile issues the same number of DMA instructions.
+    const DmaOffsets<kInt8> dmo(wave, lane, P.v_st, last * kBN, n);
     auto fetch = [&](int t) {
-        k_tile_async<kInt8>(khead, min(t, last) * kBN, kbuf(t), wave, lane);
-        v_tile_async(vhead, P.v_st, min(t, last) * kBN, n, vbuf(t), wave, lane);
+        using D = DmaOffsets<kInt8>;
+        const int kt = min(t, last);
+        const u32x4 kr = raw_rsrc(khead + (int64_t)kt * kBN * D::rowB);
+#pragma unroll
+        for (int r = 0; r < D::kn; ++r) dma16_buf(kr, dmo.k[r], kbuf(t) + (16 * wave + D::rpi * r) * D::rowB);
+        const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kBN * P.v_st);
+        const bool lt = kt == last;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dma16_buf(vr, lt ? dmo.vlast[r] : dmo.v[r], vbuf(t) + (16 * wave + 4 * r) * 256);
     };
 
     // One tile: S = K' Q'^T, online softmax, O += P V.
     auto tile = [&](int j, bool masked) {
-        fetch(j + 2);
+        fetch(j + 3);
         SVec S[2][2];
         qk_tile(kbuf(j), q, S, n32, hh);
         settle(S);
@@ -440,13 +492,14 @@ fwd_kernel(FwdParams P) {
         else
             exp_tile<false>(S, coef, m, Pb, l, j * kBN, n, hh);
         pv_tile(vbuf(j), Pb, O, lane);
-        wait_vmem_upto<kDma>();                    // tile j+1 has landed
+        wait_vmem_upto<2 * kDma>();                // tile j+1 has landed
         __syncthreads();
     };
 
     fetch(0);
     fetch(1);
-    wait_vmem_upto<kDma>();
+    fetch(2);
+    wait_vmem_upto<2 * kDma>();
     __syncthreads();
     for (int j = 0; j < last; ++j) tile(j, false);
     tile(last, ragged);

@@ -51,7 +51,7 @@ typedef enum {
     H3ATTN_OK = 0,
     H3ATTN_E_NULL = -1,         /* a required pointer is NULL                         */
     H3ATTN_E_SHAPE = -2,        /* bad N/H/sections/strides/window/scale value         */
-    H3ATTN_E_UNSUPPORTED = -3,  /* head_dim != 128, unknown format, sections not /16   */
+    H3ATTN_E_UNSUPPORTED = -3,  /* head_dim != 128, unknown format, sections not /16, V token stride > 2^24 */
     H3ATTN_E_ALIGN = -4,        /* pointer not 16-byte aligned or stride not /8 (/16) */
     H3ATTN_E_ALIAS = -5,        /* an output byte range overlaps another buffer        */
     H3ATTN_E_HIP = -6           /* the HIP runtime reported an error on launch         */
@@ -152,7 +152,8 @@ int h3attn_prep(const h3attn_problem* p,
  * q_prep/k_prep: the outputs of h3attn_prep for the same descriptor
  *            (bf16 or int8 [H][N_pad][128]); q_scales/k_scales as written
  *            by h3attn_prep (int8 format) or NULL (bf16 format).
- * v:         bf16 view [N][H][128] with strides as for q in h3attn_prep.
+ * v:         bf16 view [N][H][128] with strides as for q in h3attn_prep;
+ *            v_stride_tok above 2^24 elements returns H3ATTN_E_UNSUPPORTED.
  * o:         bf16 output view; element (n,h,c) at o + n*o_stride_tok +
  *            h*o_stride_head + c; 16-byte aligned, strides multiples of 8,
  *            and the view must not overlap itself (either o_stride_head >= 128

@@ -131,6 +131,7 @@ def test_forward_checks():
     assert fwd(p, ost=128, osh=128) == -2                # output rows overlap each other
     assert fwd(p, ost=384, osh=64) == -2
     assert fwd(p, qs=K) == -2                            # scales in bf16 format
+    assert fwd(p, vst=(1 << 24) + 8) == -3               # V token stride beyond 32-bit tile offsets
     assert fwd(p, o=F + 4096) == -5                      # output inside q'
     assert fwd(p, o=H + 384 * 10) == -5                  # output inside v
     p8 = A.problem(1000, 3, A.QK_I8_BLK64)
