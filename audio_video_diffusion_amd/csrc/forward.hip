@@ -7,9 +7,10 @@
 // the int8-QK path of "H3 Runtime Current State", Owned Performance Kernels);
 // V is read through its token-major strides and O is written token-major.
 //
-// Work decomposition (one 256-thread work-group = 4 wave64s, one per SIMD):
-// * a work-group owns 256 query rows of one head; each wave owns 64 rows as
-//   two 32-row MFMA blocks and keeps its Q' rows in registers;
+// Work decomposition: a work-group owns 256 query rows of one head.  The bf16
+// kernel (fwd8_kernel) runs eight wave64s, two per SIMD, each owning one
+// 32-row MFMA block; the int8 kernel (fwd_kernel<true>) runs four, one per
+// SIMD, each owning two.  Every wave keeps its Q' rows in registers, and:
 // * the work-group streams K'/V in tiles of 64 keys through four LDS stages,
 //   fetched three tiles ahead with buffer -> LDS DMA (buffer_load_dwordx4 ...
 //   lds: 1 KB per wave instruction, no registers in between).  K' rows land
@@ -557,13 +558,212 @@ __global__ void __launch_bounds__(256) scores_i8_kernel(ScoreParams P) {
             }
 }
 
+// ============================================================================
+// bf16 forward with two waves per SIMD: eight wave64s per work-group, each
+// owning one 32-row query block of the work-group's 256 rows (waves w and w+4
+// share a SIMD).  Per wave the state is small (O^T 64 AGPRs, Q' 32 VGPRs), so
+// two waves fit each SIMD's register file and the hardware overlaps one wave's
+// softmax with the other's matrix-core work.  Everything else follows
+// fwd_kernel: the same four LDS stages fed by buffer -> LDS DMA three tiles
+// ahead (each wave moves 8 of the 64 rows), the same permuted K' rows and
+// transposing V reads, one barrier per tile.
+// ============================================================================
+struct DmaOffsets8 {
+    uint32_t k[2], v[2], vlast[2];
+    __device__ __forceinline__ DmaOffsets8(int wave, int lane, int64_t v_st, int last_key0, int n) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int rho = 8 * wave + 4 * r + (lane >> 4);
+            const int c = (lane & 15) ^ (rho & 15);
+            k[r] = (uint32_t)(key_of_row(rho) * 256 + c * 16);
+        }
+        const uint32_t rs = (uint32_t)(v_st * 2);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int kappa = 8 * wave + 4 * r + (lane >> 4);
+            const int c = (lane & 15) ^ (4 * (kappa & 3));
+            v[r] = (uint32_t)kappa * rs + c * 16;
+            vlast[r] = (uint32_t)min(kappa, n - 1 - last_key0) * rs + c * 16;
+        }
+    }
+};
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd8_kernel(FwdParams P) {
+    constexpr int kTileB = kBN * 256;              // 16 KB: one K' or V tile
+    constexpr int kDma8 = 4;                       // DMA instructions per wave per tile
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * 2 * kTileB];
+
+    const int vb = (blockIdx.x % kXcds) * P.per_xcd + blockIdx.x / kXcds;
+    if (vb >= P.total) return;
+    const int head = vb / P.qtiles;
+    const int qt = vb % P.qtiles;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n32 = lane & 31, hh = lane >> 5;
+    const int q0 = qt * kBM + wave * 32;
+    const int n = P.n;
+    const float c = P.c;
+
+    const uint8_t* qhead = static_cast<const uint8_t*>(P.q) + (int64_t)head * P.npad * 256;
+    const uint8_t* khead = static_cast<const uint8_t*>(P.k) + (int64_t)head * P.npad * 256;
+    const uint16_t* vhead = P.v + (int64_t)head * P.v_sh;
+    auto kbuf = [&](int j) { return lds + (j % kStages) * kTileB; };
+    auto vbuf = [&](int j) { return lds + (kStages + (j % kStages)) * kTileB; };
+
+    bf16x8 q[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        q[t] = __builtin_bit_cast(bf16x8, ld16(qhead + (int64_t)(q0 + n32) * 256 + 32 * t + 16 * hh));
+
+    f32x16 O[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) O[cc] = f32x16{};
+    float m = -INFINITY, l = 0.f;
+
+    const int ntiles = (n + kBN - 1) / kBN;
+    const int last = ntiles - 1;
+    const bool ragged = (n % kBN) != 0;
+
+    const DmaOffsets8 dmo(wave, lane, P.v_st, last * kBN, n);
+    auto fetch = [&](int t) {
+        const int kt = min(t, last);
+        const u32x4 kr = raw_rsrc(khead + (int64_t)kt * kTileB);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) dma16_buf(kr, dmo.k[r], kbuf(t) + (8 * wave + 4 * r) * 256);
+        const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kBN * P.v_st);
+        const bool lt = kt == last;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) dma16_buf(vr, lt ? dmo.vlast[r] : dmo.v[r], vbuf(t) + (8 * wave + 4 * r) * 256);
+    };
+
+    const int r16 = lane & 15, g16 = lane >> 4;
+    const int rk = r16 >> 2;
+    const int v_lane_off = (8 * (g16 >> 1) + rk) * 256 + (2 * (g16 & 1) + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    auto tile = [&](int j, bool masked) {
+        fetch(j + 3);
+        // S^T of this wave's 32 queries: S[kb] = keys 32kb..32kb+31
+        f32x16 S[2];
+        {
+            const uint8_t* kb_ = kbuf(j);
+            bf16x8 a[2][8];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int rho = 32 * kb + n32;
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    a[kb][t] = *reinterpret_cast<const bf16x8*>(kb_ + rho * 256 + (((2 * t + hh) ^ (rho & 15)) * 16));
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                mfma_s(S[0], a[0][t], q[t], t == 0);
+                mfma_s(S[1], a[1][t], q[t], t == 0);
+            }
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]), "+v"(S[1]));
+        }
+        if (masked) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (j * kBN + key_of_elem(kb, e, hh) >= n) S[kb][e] = -INFINITY;
+        }
+        float mx = S[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kb][e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+        if (__any(mx > m + kRescaleLog2)) {
+            const float mm = fmaxf(m, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m - mm);
+            m = mm;
+            l *= alpha;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) scale_acc(O[cc], alpha);
+        }
+        bf16x8 Pb[2][2];
+        float rs[2] = {0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 w;
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int e = 8 * s + 2 * ii;
+                    const f32x2 f = {__builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], c, -m)),
+                                     __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], c, -m))};
+                    const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+                    rs[s] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs[s], false);
+                    w[ii] = __builtin_bit_cast(uint32_t, b);
+                }
+                Pb[kb][s] = __builtin_bit_cast(bf16x8, w);
+            }
+        l += rs[0] + rs[1];
+        // O^T += V^T P^T
+        {
+            const uint8_t* vb_ = vbuf(j);
+            typedef short i16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    bf16x8 a[4];
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) {
+                        const int off = v_lane_off + 64 * (cc ^ rk) + (32 * kb + 16 * s) * 256;
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4*)(vb_ + off));
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4*)(vb_ + off + 4 * 256));
+                        a[cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc)
+                        O[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cc], Pb[kb][s], O[cc], 0, 0, 0);
+                }
+        }
+        wait_vmem_upto<2 * kDma8>();               // tile j+1 has landed
+        __syncthreads();
+    };
+
+    fetch(0);
+    fetch(1);
+    fetch(2);
+    wait_vmem_upto<2 * kDma8>();
+    __syncthreads();
+    for (int j = 0; j < last; ++j) tile(j, false);
+    tile(last, ragged);
+    wait_vmem_all();
+
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = 1.0f / lt;
+    const int qrow = q0 + n32;
+    if (qrow < n) {
+        uint16_t* orow = P.o + (int64_t)qrow * P.o_st + (int64_t)head * P.o_sh;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x2 w = {pack_bf16x2(O[cc][4 * i] * inv, O[cc][4 * i + 1] * inv),
+                                 pack_bf16x2(O[cc][4 * i + 2] * inv, O[cc][4 * i + 3] * inv)};
+                st8(orow + 32 * cc + 8 * i + 4 * hh, w);
+            }
+    }
+}
+
 hipError_t launch_forward(const FwdParams& P, bool int8, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
     dim3 grid(kXcds * P.per_xcd), block(256);
     if (int8)
         hipLaunchKernelGGL(fwd_kernel<true>, grid, block, 0, stream, P);
     else
-        hipLaunchKernelGGL(fwd_kernel<false>, grid, block, 0, stream, P);
+        hipLaunchKernelGGL(fwd8_kernel, grid, dim3(512), 0, stream, P);
     return hipGetLastError();
 }
 
