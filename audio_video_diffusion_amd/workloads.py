@@ -71,6 +71,18 @@ WORKLOADS = (
 )
 HEADLINE = 3     # index of the 129,410-token 1344x768/124-frame workload
 
+# The pages' own block-24 attention shape: 37,810 packed tokens, 56 heads of
+# 128 ("H3 Runtime Current State", Owned Performance Kernels).  The pages give
+# only the total; the split below (a 32x24x48 video grid, 690 audio and 256 text
+# tokens) is a reading that reproduces it.  Attention cost depends on N and H
+# alone; the split only sets the RoPE positions.
+BLOCK24 = Workload("block24_37810_h56", (32, 24, 48), 690, 256, 56)
+
+# One GPU's share of the headline workload when its 24 heads are split over
+# P = 2, 4, 6, 8 GPUs (heads are independent): same tokens, H / P heads.
+SHARDS = tuple(dataclasses.replace(WORKLOADS[HEADLINE], name=f"1344x768_124f_h{24 // p}", heads=24 // p)
+               for p in (2, 4, 6, 8))
+
 
 def positions(grid, audio: int, text: int) -> np.ndarray:
     """Integer (t, h, w) positions, int32 [N, 3], in packed token order."""

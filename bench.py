@@ -35,9 +35,9 @@ PEAK_HBM_GBS = 8000.0
 # csrc/forward.hip no longer hashes to `source_sha256`, traffic is null.
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
-    "source_sha256": "f45986932c4732b3ac44f9f18dc2df898538056f49f40983e657193b5321da69",
-    "fetch_kib": 21997586.0, "fetch_scale": 2.0,
-    "write_kib": 776597.8, "write_scale": 1.0,
+    "source_sha256": "d01289f46279ed5a25c86cf2f2375b543a0271fe544e0a6a7ed7fdf34ded0a5c",
+    "fetch_kib": 13337121.4, "fetch_scale": 2.0,
+    "write_kib": 828294.5, "write_scale": 1.0,
 }
 
 
@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--cpu-heads", type=int, default=6)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the per-configuration sweep (other workloads, head shards, block-24 shape)")
     ap.add_argument("--copy-probe", type=int, default=None, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration) and exit")
     return ap.parse_args()
@@ -121,6 +123,65 @@ def cpu_baseline(wl, cfg, inp, rows_n, heads_n):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(rows)} random query rows x {len(heads)} heads of {wl.name} (all {n} keys, "
                       f"prep of every key included), fp64 numpy, {dt:.1f} s"}
+
+
+def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=None):
+    """HIP-event times (ms) of prep and forward over `steps` calls after `warmup`."""
+    import torch
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    if heads is not None:                     # one GPU's share of the heads: strided views
+        q, k, v = q[:, :heads], k[:, :heads], v[:, :heads]
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    out = []
+    for i in range(warmup + steps):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record()
+        A.prep(p, q, k, dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
+        e1.record()
+        A.forward(p, q_out, k_out, v, o, scale, qs, ks)
+        e2.record()
+        if i >= warmup:
+            out.append((e0, e1, e2))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b, _ in out], [b.elapsed_time(c) for _, b, c in out]
+
+
+def sweep(A, W, headline_dev, steps=3, warmup=1):
+    """Forward throughput of every other workload: the remaining configurations,
+    the headline's per-GPU head shards and the pages' block-24 shape."""
+    import statistics
+    import torch
+    scale = 1.0 / math.sqrt(128.0)
+    rows = []
+    jobs = [(i, W.WORKLOADS[i], None) for i in range(len(W.WORKLOADS)) if i != W.HEADLINE]
+    jobs += [(W.HEADLINE, w, w.heads) for w in W.SHARDS]
+    jobs += [(100, W.BLOCK24, None)]
+    for cfg, wl, shard_heads in jobs:
+        print(f"[bench] sweep {wl.name}: N={wl.n_tokens} H={wl.heads}", file=sys.stderr, flush=True)
+        if shard_heads is None:
+            dev = W.device_inputs(W.make_inputs(cfg, wl, threads=16))
+        else:
+            dev = headline_dev
+        fmt = A.QK_I8_BLK64 if wl.qk_int8 else A.QK_BF16
+        p = A.problem(wl.n_tokens, wl.heads, fmt)
+        q_out, k_out, qs, ks = A.alloc_prepped(p)
+        o = torch.empty((wl.n_tokens, wl.heads, 128), dtype=torch.bfloat16, device="cuda")
+        prep_ms, fwd_ms = time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, shard_heads)
+        med = statistics.median(fwd_ms)
+        tf = wl.flops / (med * 1e-3) / 1e12
+        row = {"workload": wl.name, "n_tokens": wl.n_tokens, "heads": wl.heads,
+               "qk": "int8" if wl.qk_int8 else "bf16", "steps": steps,
+               "forward_ms": {"median": round(med, 4), "min": round(min(fwd_ms), 4), "max": round(max(fwd_ms), 4)},
+               "prep_ms": round(statistics.median(prep_ms), 4),
+               "forward_tflops": round(tf, 2), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+        if wl.qk_int8:
+            # half the work (Q K^T) at the int8 rate, half (P V) at the bf16 rate
+            ideal_ms = (wl.flops / 2 / (PEAK_INT8_TOPS * 1e12) + wl.flops / 2 / (PEAK_BF16_TFLOPS * 1e12)) * 1e3
+            row["pct_mixed_peak"] = round(100 * ideal_ms / med, 2)
+        rows.append(row)
+        del dev, q_out, k_out, qs, ks, o
+        torch.cuda.empty_cache()
+    return rows
 
 
 def main():
@@ -217,6 +278,12 @@ def main():
                      "traffic": forward_traffic(wl.name),
                      "algorithmic_bytes": 4 * n * h * 128 * 2},
     }
+    fwd_all = [b.elapsed_time(c) for _, b, c in timed]
+    res["kernels"]["forward_ms_min"] = round(min(fwd_all), 4)
+    res["kernels"]["forward_ms_max"] = round(max(fwd_all), 4)
+    res["kernels"]["forward_ms_median"] = round(sorted(fwd_all)[len(fwd_all) // 2], 4)
+    if not args.headline_only and args.config is None:
+        res["per_config"] = sweep(A, W, dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, cfg, inp, args.cpu_rows, args.cpu_heads)

@@ -3,6 +3,8 @@
 Small cases are compared element by element over all outputs; the full-size
 workloads on sampled rows and heads, plus closed forms that hold at any size.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -217,6 +219,38 @@ def test_full_workload_sampled_rows_bf16(cfg):
         all_ref.append(ref)
     check(np.stack(all_got), np.stack(all_ref), what=f"{wl.name} sampled")
     assert torch.isfinite(o.float()).all()
+
+
+def test_block24_shape_sampled_rows_bf16():
+    # the pages' own block-24 attention shape: 37,810 tokens, 56 heads
+    wl = W.BLOCK24
+    print(f"    {wl.name} N={wl.n_tokens} H={wl.heads}", flush=True)
+    inp = W.make_inputs(100, wl)
+    p = problem_for(wl)
+    dev = W.device_inputs(inp)
+    q_out, k_out, _, _ = run_prep(p, dev)
+    o = run_forward(p, q_out, k_out, dev["v"])
+    rows = sample_rows(wl, n_random=64)
+    got_rows = f64(o[torch.from_numpy(rows).cuda()])
+    heads = (0, 27, 55)
+    ref = np.stack([oracle_rows_bf16(inp, h, rows) for h in heads])
+    check(np.stack([got_rows[:, h, :] for h in heads]), ref, what=f"{wl.name} sampled")
+    assert torch.isfinite(o.float()).all()
+
+
+def test_head_shard_matches_full_heads():
+    # one GPU's share of the heads (strided views of the full tensors) gives
+    # bit-identical rows to the same heads of the full problem
+    wl = W.ragged_workload(3000, 8)
+    inp = W.make_inputs(61, wl)
+    dev = W.device_inputs(inp)
+    full = run_forward(problem_for(wl), *run_prep(problem_for(wl), dev)[:2], dev["v"])
+    part = dataclasses.replace(wl, heads=3)
+    view = {**dev, "q": dev["q"][:, :3], "k": dev["k"][:, :3], "v": dev["v"][:, :3]}
+    ps = problem_for(part)
+    q_out, k_out, _, _ = run_prep(ps, view)
+    o = run_forward(ps, q_out, k_out, view["v"])
+    assert torch.equal(o, full[:, :3])
 
 
 # ---------------------------------------------------------------------------

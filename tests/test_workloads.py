@@ -67,3 +67,14 @@ def test_ragged_workload_counts():
         wl = W.ragged_workload(n, 2)
         assert wl.n_tokens == n
         assert W.positions(wl.grid, wl.audio, wl.text).shape == (n, 3)
+
+
+def test_block24_and_shard_shapes():
+    # the block-24 shape is the pages' canonical 37,810-token, 56-head block
+    # (the same figures that fix the 517 MiB V tensor above)
+    v = _golden()[1]["v_bf16_mib"]
+    assert (W.BLOCK24.n_tokens, W.BLOCK24.heads) == (v["tokens"], v["heads"])
+    # head shards keep every token and divide the 24 heads evenly
+    head = W.WORKLOADS[W.HEADLINE]
+    assert [s.heads for s in W.SHARDS] == [12, 6, 4, 3]
+    assert all(s.n_tokens == head.n_tokens and s.grid == head.grid for s in W.SHARDS)
