@@ -36,6 +36,7 @@
 // * the blockIdx -> (head, query tile) map keeps the work-groups that one XCD
 //   runs at a time on adjacent query tiles of one head, so K'/V tiles are
 //   shared through that XCD's L2.
+#include <cfloat>
 #include <type_traits>
 
 #include "common.h"
@@ -568,14 +569,19 @@ __global__ void __launch_bounds__(256) scores_i8_kernel(ScoreParams P) {
 // ahead (each wave moves 8 of the 64 rows), the same permuted K' rows and
 // transposing V reads, one barrier per tile.
 // ============================================================================
+template <bool kInt8>
 struct DmaOffsets8 {
-    uint32_t k[2], v[2], vlast[2];
+    static constexpr int kRowB = kInt8 ? 128 : 256;   // K' row bytes
+    static constexpr int kN = kInt8 ? 1 : 2;          // K' DMA instructions per wave
+    uint32_t k[kN], v[2], vlast[2];
     __device__ __forceinline__ DmaOffsets8(int wave, int lane, int64_t v_st, int last_key0, int n) {
+        // each wave moves K' rows 8w..8w+7: 8 (int8) or 4 (bf16) rows per instruction
+        constexpr int cpr = kRowB / 16, rpi = 64 / cpr;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int rho = 8 * wave + 4 * r + (lane >> 4);
-            const int c = (lane & 15) ^ (rho & 15);
-            k[r] = (uint32_t)(key_of_row(rho) * 256 + c * 16);
+        for (int r = 0; r < kN; ++r) {
+            const int rho = 8 * wave + rpi * r + lane / cpr;
+            const int c = (lane % cpr) ^ (rho & (cpr - 1));
+            k[r] = (uint32_t)(key_of_row(rho) * kRowB + c * 16);
         }
         const uint32_t rs = (uint32_t)(v_st * 2);
 #pragma unroll
@@ -588,11 +594,14 @@ struct DmaOffsets8 {
     }
 };
 
+template <bool kInt8>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd8_kernel(FwdParams P) {
-    constexpr int kTileB = kBN * 256;              // 16 KB: one K' or V tile
-    constexpr int kDma8 = 4;                       // DMA instructions per wave per tile
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * 2 * kTileB];
+    using D = DmaOffsets8<kInt8>;
+    constexpr int kKTileB = kBN * D::kRowB;        // 16 KB (bf16) or 8 KB (int8)
+    constexpr int kVTileB = kBN * 256;             // 16 KB
+    constexpr int kDma8 = D::kN + 2;               // DMA instructions per wave per tile
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * (kKTileB + kVTileB)];
 
     const int vb = (blockIdx.x % kXcds) * P.per_xcd + blockIdx.x / kXcds;
     if (vb >= P.total) return;
@@ -604,18 +613,23 @@ fwd8_kernel(FwdParams P) {
     const int n32 = lane & 31, hh = lane >> 5;
     const int q0 = qt * kBM + wave * 32;
     const int n = P.n;
-    const float c = P.c;
 
-    const uint8_t* qhead = static_cast<const uint8_t*>(P.q) + (int64_t)head * P.npad * 256;
-    const uint8_t* khead = static_cast<const uint8_t*>(P.k) + (int64_t)head * P.npad * 256;
+    const uint8_t* qhead = static_cast<const uint8_t*>(P.q) + (int64_t)head * P.npad * D::kRowB;
+    const uint8_t* khead = static_cast<const uint8_t*>(P.k) + (int64_t)head * P.npad * D::kRowB;
     const uint16_t* vhead = P.v + (int64_t)head * P.v_sh;
-    auto kbuf = [&](int j) { return lds + (j % kStages) * kTileB; };
-    auto vbuf = [&](int j) { return lds + (kStages + (j % kStages)) * kTileB; };
+    auto kbuf = [&](int j) { return lds + (j % kStages) * kKTileB; };
+    auto vbuf = [&](int j) { return lds + kStages * kKTileB + (j % kStages) * kVTileB; };
 
-    bf16x8 q[8];
+    // this wave's 32 query rows as MFMA B operands
+    using QOp = typename std::conditional<kInt8, i32x4, bf16x8>::type;
+    constexpr int kSteps = kInt8 ? 4 : 8;          // d-steps of 32 (int8) or 16 (bf16)
+    QOp q[kSteps];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-        q[t] = __builtin_bit_cast(bf16x8, ld16(qhead + (int64_t)(q0 + n32) * 256 + 32 * t + 16 * hh));
+    for (int t = 0; t < kSteps; ++t)
+        q[t] = __builtin_bit_cast(QOp, ld16(qhead + (int64_t)(q0 + n32) * D::kRowB + 32 * t + 16 * hh));
+    float qscale = 1.f;
+    if constexpr (kInt8) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
+    const float* kscale = kInt8 ? P.ks + (int64_t)head * P.nblk : nullptr;
 
     f32x16 O[4];
 #pragma unroll
@@ -626,12 +640,13 @@ fwd8_kernel(FwdParams P) {
     const int last = ntiles - 1;
     const bool ragged = (n % kBN) != 0;
 
-    const DmaOffsets8 dmo(wave, lane, P.v_st, last * kBN, n);
+    const D dmo(wave, lane, P.v_st, last * kBN, n);
     auto fetch = [&](int t) {
         const int kt = min(t, last);
-        const u32x4 kr = raw_rsrc(khead + (int64_t)kt * kTileB);
+        const u32x4 kr = raw_rsrc(khead + (int64_t)kt * kKTileB);
 #pragma unroll
-        for (int r = 0; r < 2; ++r) dma16_buf(kr, dmo.k[r], kbuf(t) + (8 * wave + 4 * r) * 256);
+        for (int r = 0; r < D::kN; ++r)
+            dma16_buf(kr, dmo.k[r], kbuf(t) + (8 * wave + (kInt8 ? 8 : 4) * r) * D::kRowB);
         const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kBN * P.v_st);
         const bool lt = kt == last;
 #pragma unroll
@@ -648,8 +663,28 @@ fwd8_kernel(FwdParams P) {
         fetch(j + 3);
         // S^T of this wave's 32 queries: S[kb] = keys 32kb..32kb+31
         f32x16 S[2];
-        {
-            const uint8_t* kb_ = kbuf(j);
+        const uint8_t* kb_ = kbuf(j);
+        if constexpr (kInt8) {
+            i32x4 a[2][4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int rho = 32 * kb + n32;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    a[kb][t] = *reinterpret_cast<const i32x4*>(kb_ + rho * 128 + (((2 * t + hh) ^ (rho & 7)) * 16));
+            }
+            i32x16 Si[2] = {i32x16{}, i32x16{}};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                Si[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0][t], q[t], Si[0], 0, 0, 0);
+                Si[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[1][t], q[t], Si[1], 0, 0, 0);
+            }
+            // |S| <= 127 * 127 * 128 < 2^24: exact in fp32
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) S[kb][e] = (float)Si[kb][e];
+        } else {
             bf16x8 a[2][8];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -665,19 +700,22 @@ fwd8_kernel(FwdParams P) {
             }
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]), "+v"(S[1]));
         }
+        // base-2 logit scale of this tile (int8: times the two block scales)
+        const float coef = kInt8 ? P.c * qscale * kscale[j] : P.c;
         if (masked) {
+            // keys >= N: the most negative finite score for the max, probability 0 below
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    if (j * kBN + key_of_elem(kb, e, hh) >= n) S[kb][e] = -INFINITY;
+                    if (j * kBN + key_of_elem(kb, e, hh) >= n) S[kb][e] = -FLT_MAX;
         }
         float mx = S[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kb][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * coef;
         if (__any(mx > m + kRescaleLog2)) {
             const float mm = fmaxf(m, mx);
             const float alpha = __builtin_amdgcn_exp2f(m - mm);
@@ -696,8 +734,13 @@ fwd8_kernel(FwdParams P) {
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
                     const int e = 8 * s + 2 * ii;
-                    const f32x2 f = {__builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], c, -m)),
-                                     __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], c, -m))};
+                    float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -m));
+                    float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], coef, -m));
+                    if (masked) {
+                        if (j * kBN + key_of_elem(kb, e, hh) >= n) x0 = 0.f;
+                        if (j * kBN + key_of_elem(kb, e + 1, hh) >= n) x1 = 0.f;
+                    }
+                    const f32x2 f = {x0, x1};
                     const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
                     rs[s] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs[s], false);
                     w[ii] = __builtin_bit_cast(uint32_t, b);
@@ -761,9 +804,9 @@ hipError_t launch_forward(const FwdParams& P, bool int8, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
     dim3 grid(kXcds * P.per_xcd), block(256);
     if (int8)
-        hipLaunchKernelGGL(fwd_kernel<true>, grid, block, 0, stream, P);
+        hipLaunchKernelGGL(fwd8_kernel<true>, grid, dim3(512), 0, stream, P);
     else
-        hipLaunchKernelGGL(fwd8_kernel, grid, dim3(512), 0, stream, P);
+        hipLaunchKernelGGL(fwd8_kernel<false>, grid, dim3(512), 0, stream, P);
     return hipGetLastError();
 }
 
