@@ -7,15 +7,18 @@
 // the int8-QK path of "H3 Runtime Current State", Owned Performance Kernels);
 // V is read through its token-major strides and O is written token-major.
 //
-// Work decomposition: a work-group owns 256 query rows of one head.  The bf16
-// kernel (fwd8_kernel) runs eight wave64s, two per SIMD, each owning one
-// 32-row MFMA block; the int8 kernel (fwd_kernel<true>) runs four, one per
-// SIMD, each owning two.  Every wave keeps its Q' rows in registers, and:
+// Work decomposition (fwd8_kernel, bf16 and int8 Q/K):
+// * a work-group of eight wave64s owns 256 query rows of one head; each wave
+//   owns one 32-row block and keeps its Q' rows in registers.  Waves w and
+//   w+4 share a SIMD: per wave the state is small (O^T in 64 AGPRs), so two
+//   waves fit each SIMD's register file and the hardware overlaps one wave's
+//   softmax with the other's matrix-core work;
 // * the work-group streams K'/V in tiles of 64 keys through four LDS stages,
 //   fetched three tiles ahead with buffer -> LDS DMA (buffer_load_dwordx4 ...
-//   lds: 1 KB per wave instruction, no registers in between).  K' rows land
-//   permuted, V rows stay row-major; 16-byte chunks are XOR-swizzled so the
-//   operand reads below hit every LDS bank.  One barrier per tile;
+//   lds: 1 KB per wave instruction, no registers in between; each wave moves
+//   8 of the 64 rows).  K' rows land permuted, V rows stay row-major; 16-byte
+//   chunks are XOR-swizzled so the operand reads hit every LDS bank.  One
+//   barrier per tile;
 // * everything is computed transposed so that one lane owns one query column:
 //     S^T (keys x queries) = K' Q'^T     with v_mfma_f32_32x32x16_bf16
 //                                        (int8: v_mfma_i32_32x32x32_i8)
@@ -36,6 +39,9 @@
 // * the blockIdx -> (head, query tile) map keeps the work-groups that one XCD
 //   runs at a time on adjacent query tiles of one head, so K'/V tiles are
 //   shared through that XCD's L2.
+//
+// scores_i8_kernel is a test hook: the exact int32 Q K^T of the int8 path for
+// a window of rows and keys, computed with the same operand layout.
 #include <cfloat>
 #include <type_traits>
 
@@ -50,15 +56,9 @@ constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;
 
 // LDS tile sizes in bytes; four stages of each are in flight
-template <bool kInt8> struct Lds {
-    static constexpr int kRow = kInt8 ? 128 : 256;            // K' row, unpadded (swizzled)
-    static constexpr int kBytes = kBN * kRow;
-    static constexpr int vRow = kHeadDim * 2;                 // V row [key][d], unpadded (swizzled)
-    static constexpr int vBytes = kBN * vRow;
-    static constexpr int kDmaPerWave = kBytes / 1024 / 4;     // global_load_lds_dwordx4 per wave
-    static constexpr int vDmaPerWave = vBytes / 1024 / 4;
-};
-constexpr int kStages = 4;
+constexpr int kStages = 4;          // LDS stages of the K'/V stream
+// K' tile of the int8 scores test hook: 64 rows of 128 bytes
+constexpr int kKTileI8 = kBN * 128;
 
 // Tile-local key held by LDS row rho: the 32x32 accumulator row order
 // (rows 8i + 4h + j) mapped so that accumulator element 8s+e of lane half h
@@ -100,46 +100,15 @@ __device__ __forceinline__ void dma16_buf(const u32x4& rsrc, uint32_t voff, cons
                  :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
 }
 
-// Per-lane byte offsets of one wave's share of a K' tile and of a V tile.
-// K': slot c of LDS row rho holds 16-byte chunk c ^ (rho mod chunks-per-row)
-// of key key_of_row(rho).  V: slot c of row kappa holds chunk c ^ 4(kappa mod
-// 4).  vlast clamps V rows past N to row N-1 for the last tile (first key
-// last_key0): their probabilities are exactly 0, any finite value will do.
-template <bool kInt8>
-struct DmaOffsets {
-    static constexpr int rowB = Lds<kInt8>::kRow;
-    static constexpr int cpr = rowB / 16;
-    static constexpr int rpi = 64 / cpr;
-    static constexpr int kn = 16 / rpi;
-    uint32_t k[kn], v[4], vlast[4];
-    __device__ __forceinline__ DmaOffsets(int wave, int lane, int64_t v_st, int last_key0, int n) {
-#pragma unroll
-        for (int r = 0; r < kn; ++r) {
-            const int rho = 16 * wave + rpi * r + lane / cpr;
-            const int c = (lane % cpr) ^ (rho & (cpr - 1));
-            k[r] = (uint32_t)(key_of_row(rho) * rowB + c * 16);
-        }
-        const uint32_t rs = (uint32_t)(v_st * 2);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int kappa = 16 * wave + 4 * r + (lane >> 4);
-            const int c = (lane & 15) ^ (4 * (kappa & 3));
-            v[r] = (uint32_t)kappa * rs + c * 16;
-            vlast[r] = (uint32_t)min(kappa, n - 1 - last_key0) * rs + c * 16;
-        }
-    }
-};
-
-// ---- K' tile: global -> LDS directly ---------------------------------------
+// ---- K' tile of the scores test hook: global -> LDS directly ---------------
 
 // Slot c of LDS row rho holds 16-byte chunk c ^ (rho mod chunks-per-row) of the
 // row's key: lanes reading one chunk of 8 (16) consecutive rows hit distinct banks.
-template <bool kInt8>
 __device__ __forceinline__ void k_tile_async(const uint8_t* khead, int key0, uint8_t* kbuf, int wave,
                                              int lane) {
-    constexpr int rowB = Lds<kInt8>::kRow;
-    constexpr int cpr = rowB / 16;          // chunks per row: 16 (bf16) or 8 (int8)
-    constexpr int rpi = 64 / cpr;           // rows per wave instruction: 4 or 8
+    constexpr int rowB = 128;                // int8 K' row
+    constexpr int cpr = rowB / 16;          // chunks per row
+    constexpr int rpi = 64 / cpr;           // rows per wave instruction
 #pragma unroll
     for (int r = 0; r < 16 / rpi; ++r) {    // each wave fills 16 rows
         const int row0 = 16 * wave + rpi * r;
@@ -150,7 +119,7 @@ __device__ __forceinline__ void k_tile_async(const uint8_t* khead, int key0, uin
     }
 }
 
-// ---- S^T = K' Q'^T for one tile: S[kb][qb] is keys 32kb.. x queries 32qb.. --
+// ---- S^T = K' Q'^T ---------------------------------------------------------
 
 // S accumulates in arch VGPRs (the softmax reads it with VALU ops) while Q'
 // stays in AGPRs: these MFMAs are issued as inline asm to pin the register
@@ -161,37 +130,6 @@ __device__ __forceinline__ void mfma_s(f32x16& d, const bf16x8& a, const bf16x8&
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
     else
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-}
-
-// The compiler does not see the latency of the asm MFMAs above: before a VALU
-// op reads their result, 24 wait states (more than the 8-pass XDL -> VALU
-// requirement) are inserted, ordered after the MFMAs through the operand.
-__device__ __forceinline__ void settle(f32x16 (&S)[2][2]) {
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+v"(S[0][0]), "+v"(S[0][1]), "+v"(S[1][0]), "+v"(S[1][1]));
-}
-__device__ __forceinline__ void settle(i32x16 (&)[2][2]) {}
-
-__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const bf16x8 (&q)[2][8], f32x16 (&S)[2][2],
-                                        int n32, int hh) {
-    // all 16 A operands first (they sit in AGPRs), so LDS latency overlaps
-    bf16x8 a[2][8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const int rho = 32 * kb + n32;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int slot = (2 * t + hh) ^ (rho & 15);
-            a[kb][t] = *reinterpret_cast<const bf16x8*>(kbuf + rho * 256 + slot * 16);
-        }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            mfma_s(S[kb][0], a[kb][t], q[0][t], t == 0);
-            mfma_s(S[kb][1], a[kb][t], q[1][t], t == 0);
-        }
 }
 
 __device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const i32x4 (&q)[2][4], i32x16 (&S)[2][2],
@@ -211,15 +149,7 @@ __device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const i32x4 (&q)[2]
     }
 }
 
-// Q' rows of one wave as MFMA B operands: lane (n32, hh) holds row q0+32qb+n32.
-__device__ __forceinline__ void load_q(const uint8_t* qhead, int q0, int n32, int hh, bf16x8 (&q)[2][8]) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            q[qb][t] = __builtin_bit_cast(bf16x8, ld16(qhead + (int64_t)(q0 + 32 * qb + n32) * 256 + 32 * t + 16 * hh));
-}
-
+// int8 Q' codes of one wave's 64 rows as MFMA B operands: lane (n32, hh) holds row q0+32qb+n32.
 __device__ __forceinline__ void load_q(const uint8_t* qhead, int q0, int n32, int hh, i32x4 (&q)[2][4]) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -228,120 +158,9 @@ __device__ __forceinline__ void load_q(const uint8_t* qhead, int q0, int n32, in
             q[qb][t] = __builtin_bit_cast(i32x4, ld16(qhead + (int64_t)(q0 + 32 * qb + n32) * 128 + 32 * t + 16 * hh));
 }
 
-// ---- softmax pieces ---------------------------------------------------------
-
-__device__ __forceinline__ float to_f(float x) { return x; }
-__device__ __forceinline__ float to_f(int x) { return (float)x; }
-__device__ __forceinline__ float neg_inf_of(float) { return -INFINITY; }
-__device__ __forceinline__ int neg_inf_of(int) { return INT32_MIN; }
-__device__ __forceinline__ float vmax(float a, float b) { return __builtin_fmaxf(a, b); }
-__device__ __forceinline__ int vmax(int a, int b) { return a > b ? a : b; }
-
 // Tile-local key of accumulator element e of block kb for lane half hh.
 __device__ __forceinline__ int key_of_elem(int kb, int e, int hh) {
     return 32 * kb + 16 * (e >> 3) + 8 * hh + (e & 7);
-}
-
-template <typename V>
-__device__ __forceinline__ void mask_tile(V (&S)[2][2], int key0, int n, int hh) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (key0 + key_of_elem(kb, e, hh) >= n) S[kb][qb][e] = neg_inf_of(S[kb][qb][e]);
-}
-
-// Scaled (base-2) row max of query block qb over the whole tile (both lane halves).
-template <typename V>
-__device__ __forceinline__ float row_max(const V (&S)[2][2], int qb, float coef) {
-    auto mx = S[0][qb][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = vmax(mx, S[kb][qb][e]);
-    float f = to_f(mx) * coef;
-    return fmaxf(f, __shfl_xor(f, 32));
-}
-
-// P = exp2(S * coef - m) rounded to bf16 as the P V operands; l += row sums of
-// those bf16 values (two at a time: a bf16 dot product against (1, 1)).
-template <bool kMask, typename V>
-__device__ __forceinline__ void exp_tile(const V (&S)[2][2], float coef, const float (&m)[2],
-                                         bf16x8 (&Pb)[2][2][2], float (&l)[2], int key0, int n, int hh) {
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        float rs[2] = {0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            float p[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(to_f(S[kb][qb][e]), coef, -m[qb]));
-                if constexpr (kMask) {
-                    // keys >= N: probability exactly 0 (also when coef == 0)
-                    if (key0 + key_of_elem(kb, e, hh) >= n) p[e] = 0.f;
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                // Each pair goes through a bf16x2 value of its own: a bit_cast of
-                // a u32x4 element to bf16x2 feeding the dot product was
-                // miscompiled (every dot read element 0).
-                u32x4 w;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x2 f = {p[8 * s + 2 * i], p[8 * s + 2 * i + 1]};
-                    const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
-                    rs[s] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs[s], false);
-                    w[i] = __builtin_bit_cast(uint32_t, b);
-                }
-                Pb[qb][kb][s] = __builtin_bit_cast(bf16x8, w);
-            }
-        }
-        l[qb] += rs[0] + rs[1];
-    }
-}
-
-// O^T += V^T P^T for one tile.  The A operand (8 consecutive keys of one d
-// column) comes from the row-major V tile through ds_read_b64_tr_b16: in each
-// 16-lane group, output lane i, slot k is element i%4 of the 4 read by lane
-// 4k + i/4, so lane r reads row (key base + r/4), columns D0 + 4(r%4)..+3.
-__device__ __forceinline__ void pv_tile(const uint8_t* vbuf, const bf16x8 (&Pb)[2][2][2], f32x16 (&O)[2][4],
-                                        int lane) {
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    const int r = lane & 15, g = lane >> 4;
-    const int hhl = g >> 1, dh = g & 1, rk = r >> 2;
-    // byte offset of this lane inside a 4-row group, without the column block c
-    const int lane_off = (8 * hhl + rk) * 256 + (2 * dh + ((r & 3) >> 1)) * 16 + 8 * (r & 1);
-    bf16x8 a[4][2][2];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int off_c = lane_off + 64 * (c ^ rk);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int off = off_c + (32 * kb + 16 * s) * 256;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4*)(vbuf + off));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4*)(vbuf + off + 4 * 256));
-                a[c][kb][s] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                O[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][kb][s], Pb[0][kb][s], O[0][c], 0, 0, 0);
-                O[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][kb][s], Pb[1][kb][s], O[1][c], 0, 0, 0);
-            }
 }
 
 // acc *= alpha with acc pinned to the accumulation registers (AGPRs): the rare
@@ -366,39 +185,6 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
     }
 }
 
-// Raise the running max when a row's new max exceeds it by more than 2^8.
-__device__ __forceinline__ void maybe_rescale(const float (&mx)[2], float (&m)[2], float (&l)[2],
-                                              f32x16 (&O)[2][4]) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        if (__any(mx[qb] > m[qb] + kRescaleLog2)) {
-            const float mm = fmaxf(m[qb], mx[qb]);
-            const float alpha = __builtin_amdgcn_exp2f(m[qb] - mm);
-            m[qb] = mm;
-            l[qb] *= alpha;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) scale_acc(O[qb][c], alpha);
-        }
-    }
-}
-
-// Empty asm statements that fix a value's register class at this point: Q' (an
-// MFMA operand only) lives in AGPRs, S (read by the softmax VALU ops) in VGPRs.
-template <typename T, int A, int B>
-__device__ __forceinline__ void pin_agpr(T (&x)[A][B]) {
-#pragma unroll
-    for (int a = 0; a < A; ++a)
-#pragma unroll
-        for (int b = 0; b < B; ++b) asm volatile("" : "+a"(x[a][b]));
-}
-template <typename T, int A, int B>
-__device__ __forceinline__ void pin_vgpr(T (&x)[A][B]) {
-#pragma unroll
-    for (int a = 0; a < A; ++a)
-#pragma unroll
-        for (int b = 0; b < B; ++b) asm volatile("" : "+v"(x[a][b]));
-}
-
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most kOutstanding of this wave's DMA instructions are still in
 // flight (vmcnt retires in issue order): with the two newest fetches allowed
@@ -412,126 +198,8 @@ __device__ __forceinline__ void wait_vmem_upto() {
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool kInt8>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-fwd_kernel(FwdParams P) {
-    using L = Lds<kInt8>;
-    using QReg = typename std::conditional<kInt8, i32x4[2][4], bf16x8[2][8]>::type;
-    using SVec = typename std::conditional<kInt8, i32x16, f32x16>::type;
-    constexpr int kDma = L::kDmaPerWave + L::vDmaPerWave;      // per wave per tile
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * (L::kBytes + L::vBytes)];
-
-    const int vb = (blockIdx.x % kXcds) * P.per_xcd + blockIdx.x / kXcds;
-    if (vb >= P.total) return;                     // whole work-group, before any barrier
-    const int head = vb / P.qtiles;
-    const int qt = vb % P.qtiles;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n32 = lane & 31, hh = lane >> 5;
-    const int q0 = qt * kBM + wave * 64;
-    const int n = P.n;
-
-    constexpr int elt = kInt8 ? 1 : 2;
-    const uint8_t* qhead = static_cast<const uint8_t*>(P.q) + (int64_t)head * P.npad * kHeadDim * elt;
-    const uint8_t* khead = static_cast<const uint8_t*>(P.k) + (int64_t)head * P.npad * kHeadDim * elt;
-    const uint16_t* vhead = P.v + (int64_t)head * P.v_sh;
-    const float* kscale = kInt8 ? P.ks + (int64_t)head * P.nblk : nullptr;
-    auto kbuf = [&](int j) { return lds + (j % kStages) * L::kBytes; };
-    auto vbuf = [&](int j) { return lds + kStages * L::kBytes + (j % kStages) * L::vBytes; };
-
-    QReg q;
-    load_q(qhead, q0, n32, hh, q);
-    pin_agpr(q);
-    float qscale = 1.f;
-    if constexpr (kInt8) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
-    auto coef_of = [&](int j) -> float {
-        if constexpr (kInt8) return P.c * qscale * kscale[j];
-        else return P.c;
-    };
-
-    f32x16 O[2][4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) O[qb][c] = f32x16{};
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-
-    const int ntiles = (n + kBN - 1) / kBN;
-    const int last = ntiles - 1;
-    const bool ragged = (n % kBN) != 0;
-    // K'_t and V_t land in stage t % 4, fetched three tiles ahead.  Indices past the
-    // last tile re-fetch the last tile into a stage nobody reads any more, so
-    // every tile issues the same number of DMA instructions.
-    const DmaOffsets<kInt8> dmo(wave, lane, P.v_st, last * kBN, n);
-    auto fetch = [&](int t) {
-        using D = DmaOffsets<kInt8>;
-        const int kt = min(t, last);
-        const u32x4 kr = raw_rsrc(khead + (int64_t)kt * kBN * D::rowB);
-#pragma unroll
-        for (int r = 0; r < D::kn; ++r) dma16_buf(kr, dmo.k[r], kbuf(t) + (16 * wave + D::rpi * r) * D::rowB);
-        const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kBN * P.v_st);
-        const bool lt = kt == last;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dma16_buf(vr, lt ? dmo.vlast[r] : dmo.v[r], vbuf(t) + (16 * wave + 4 * r) * 256);
-    };
-
-    // One tile: S = K' Q'^T, online softmax, O += P V.
-    auto tile = [&](int j, bool masked) {
-        fetch(j + 3);
-        SVec S[2][2];
-        qk_tile(kbuf(j), q, S, n32, hh);
-        settle(S);
-        if (masked) mask_tile(S, j * kBN, n, hh);
-        const float coef = coef_of(j);
-        float mx[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) mx[qb] = row_max(S, qb, coef);
-        maybe_rescale(mx, m, l, O);
-        bf16x8 Pb[2][2][2];
-        if (masked)
-            exp_tile<true>(S, coef, m, Pb, l, j * kBN, n, hh);
-        else
-            exp_tile<false>(S, coef, m, Pb, l, j * kBN, n, hh);
-        pv_tile(vbuf(j), Pb, O, lane);
-        wait_vmem_upto<2 * kDma>();                // tile j+1 has landed
-        __syncthreads();
-    };
-
-    fetch(0);
-    fetch(1);
-    fetch(2);
-    wait_vmem_upto<2 * kDma>();
-    __syncthreads();
-    for (int j = 0; j < last; ++j) tile(j, false);
-    tile(last, ragged);
-    wait_vmem_all();                               // no DMA may land after the work-group ends
-
-    // epilogue: O^T / l -> bf16, lane (n32, hh) holds d = 32c + 8i + 4hh + j of its query
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float lt = l[qb] + __shfl_xor(l[qb], 32);
-        const float inv = 1.0f / lt;
-        const int qrow = q0 + 32 * qb + n32;
-        if (qrow < n) {
-            uint16_t* orow = P.o + (int64_t)qrow * P.o_st + (int64_t)head * P.o_sh;
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x2 w = {pack_bf16x2(O[qb][c][4 * i] * inv, O[qb][c][4 * i + 1] * inv),
-                                     pack_bf16x2(O[qb][c][4 * i + 2] * inv, O[qb][c][4 * i + 3] * inv)};
-                    st8(orow + 32 * c + 8 * i + 4 * hh, w);
-                }
-        }
-    }
-}
-
-// ---- exact int32 scores of the int8 path (test hook), same tile routines ----
-
 __global__ void __launch_bounds__(256) scores_i8_kernel(ScoreParams P) {
-    using L = Lds<true>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[L::kBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kKTileI8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n32 = lane & 31, hh = lane >> 5;
     const int qbase = (P.row0 / kBM) * kBM + blockIdx.y * kBM;
@@ -540,7 +208,7 @@ __global__ void __launch_bounds__(256) scores_i8_kernel(ScoreParams P) {
 
     i32x4 q[2][4];
     load_q(P.qhead, q0, n32, hh, q);
-    k_tile_async<true>(P.khead, kbase, lds, wave, lane);
+    k_tile_async(P.khead, kbase, lds, wave, lane);
     wait_vmem_all();
     __syncthreads();
     i32x16 S[2][2];
@@ -560,14 +228,7 @@ __global__ void __launch_bounds__(256) scores_i8_kernel(ScoreParams P) {
 }
 
 // ============================================================================
-// bf16 forward with two waves per SIMD: eight wave64s per work-group, each
-// owning one 32-row query block of the work-group's 256 rows (waves w and w+4
-// share a SIMD).  Per wave the state is small (O^T 64 AGPRs, Q' 32 VGPRs), so
-// two waves fit each SIMD's register file and the hardware overlaps one wave's
-// softmax with the other's matrix-core work.  Everything else follows
-// fwd_kernel: the same four LDS stages fed by buffer -> LDS DMA three tiles
-// ahead (each wave moves 8 of the 64 rows), the same permuted K' rows and
-// transposing V reads, one barrier per tile.
+// The forward kernel (see the file comment).
 // ============================================================================
 template <bool kInt8>
 struct DmaOffsets8 {
