@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libh3attn.so")
-SOURCES = ("api.hip", "prep.hip", "forward.hip")
+SOURCES = ("api.hip", "prep.hip", "prep_v.hip", "forward.hip")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code.  No fast-math: the
@@ -40,7 +40,7 @@ def build(verbose: bool = False, asm: bool = False) -> str:
     cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     if asm:
         os.makedirs(os.path.join(ROOT, "_build"), exist_ok=True)
-        cmd[1:1] = ["-save-temps=obj"]
+        cmd[1:1] = ["-save-temps=cwd"]
     if verbose:
         print(" ".join(cmd), flush=True)
     cwd = os.path.join(ROOT, "_build") if asm else CSRC

@@ -100,6 +100,16 @@ size_t h3attn_scales_bytes(const h3attn_problem* p) {
     return (size_t)p->n_heads * (size_t)nblk_of(p) * sizeof(float);
 }
 
+size_t h3attn_prepped_v_bytes(const h3attn_problem* p) {
+    if (check_problem(p) != H3ATTN_OK) return 0;
+    return (size_t)p->n_heads * (size_t)npad_of(p) * 128;
+}
+
+size_t h3attn_v_scales_bytes(const h3attn_problem* p) {
+    if (check_problem(p) != H3ATTN_OK) return 0;
+    return (size_t)p->n_heads * 128 * sizeof(float);
+}
+
 int h3attn_prep(const h3attn_problem* p,
                 const void* q, int64_t q_stride_tok, int64_t q_stride_head,
                 const void* k, int64_t k_stride_tok, int64_t k_stride_head,
@@ -154,12 +164,15 @@ int h3attn_prep(const h3attn_problem* p,
     return H3ATTN_OK;
 }
 
-int h3attn_forward(const h3attn_problem* p,
-                   const void* q_prep, const void* k_prep,
-                   const float* q_scales, const float* k_scales,
-                   const void* v, int64_t v_stride_tok, int64_t v_stride_head,
-                   void* o, int64_t o_stride_tok, int64_t o_stride_head,
-                   float softmax_scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by h3attn_forward (bf16 V view) and h3attn_forward_fp8v (staged E4M3 V).
+int forward_common(const h3attn_problem* p, const void* q_prep, const void* k_prep,
+                   const float* q_scales, const float* k_scales, bool fp8v, const void* v,
+                   int64_t v_stride_tok, int64_t v_stride_head, const float* v_scales, void* o,
+                   int64_t o_stride_tok, int64_t o_stride_head, float softmax_scale, void* stream) {
     int rc = check_problem(p);
     if (rc) return rc;
     const bool i8 = p->qk_format == H3ATTN_QK_I8_BLK64;
@@ -168,12 +181,20 @@ int h3attn_forward(const h3attn_problem* p,
     if (i8 && (!q_scales || !k_scales)) return H3ATTN_E_NULL;
     if (!i8 && (q_scales || k_scales)) return H3ATTN_E_SHAPE;
     if (i8 && (!aligned(q_scales, 4) || !aligned(k_scales, 4))) return H3ATTN_E_ALIGN;
-    if ((rc = check_in_view(v, v_stride_tok, v_stride_head))) return rc;
-    if (v_stride_tok > kMaxVStrideTok) return H3ATTN_E_UNSUPPORTED;
+    const int64_t n = p->n_tokens, h = p->n_heads;
+    Range vrng;
+    if (fp8v) {
+        if (!v || !v_scales) return H3ATTN_E_NULL;
+        if (!aligned(v, 16) || !aligned(v_scales, 4)) return H3ATTN_E_ALIGN;
+        vrng = span(v, h3attn_prepped_v_bytes(p));
+    } else {
+        if ((rc = check_in_view(v, v_stride_tok, v_stride_head))) return rc;
+        if (v_stride_tok > kMaxVStrideTok) return H3ATTN_E_UNSUPPORTED;
+        vrng = view_range(v, n, h, v_stride_tok, v_stride_head, 128, 2);
+    }
     if ((rc = check_in_view(o, o_stride_tok, o_stride_head))) return rc;
     if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return H3ATTN_E_SHAPE;
 
-    const int64_t n = p->n_tokens, h = p->n_heads;
     // the output view must not overlap itself
     const bool nhd_ok = o_stride_head >= 128 && o_stride_tok >= (h - 1) * o_stride_head + 128;
     const bool hnd_ok = o_stride_tok >= 128 && o_stride_head >= (n - 1) * o_stride_tok + 128;
@@ -181,15 +202,16 @@ int h3attn_forward(const h3attn_problem* p,
 
     const size_t in_b = h3attn_prepped_qk_bytes(p), sc_b = h3attn_scales_bytes(p);
     const Range orng = view_range(o, n, h, o_stride_tok, o_stride_head, 128, 2);
-    if (overlap(orng, span(q_prep, in_b)) || overlap(orng, span(k_prep, in_b)) ||
-        overlap(orng, view_range(v, n, h, v_stride_tok, v_stride_head, 128, 2)))
+    if (overlap(orng, span(q_prep, in_b)) || overlap(orng, span(k_prep, in_b)) || overlap(orng, vrng))
         return H3ATTN_E_ALIAS;
     if (i8 && (overlap(orng, span(q_scales, sc_b)) || overlap(orng, span(k_scales, sc_b))))
         return H3ATTN_E_ALIAS;
+    if (fp8v && overlap(orng, span(v_scales, h3attn_v_scales_bytes(p)))) return H3ATTN_E_ALIAS;
 
     h3::FwdParams P{};
     P.q = q_prep; P.k = k_prep; P.qs = q_scales; P.ks = k_scales;
-    P.v = static_cast<const uint16_t*>(v); P.v_st = v_stride_tok; P.v_sh = v_stride_head;
+    P.v = static_cast<const uint16_t*>(v); P.v_st = fp8v ? 0 : v_stride_tok; P.v_sh = fp8v ? 0 : v_stride_head;
+    P.vs = v_scales;
     P.o = static_cast<uint16_t*>(o); P.o_st = o_stride_tok; P.o_sh = o_stride_head;
     P.n = (int)n; P.h = (int)h; P.npad = (int)npad_of(p); P.nblk = (int)nblk_of(p);
     P.qtiles = (int)((n + 255) / 256);
@@ -198,7 +220,51 @@ int h3attn_forward(const h3attn_problem* p,
     P.total = (int)total;
     P.per_xcd = (int)((total + 7) / 8);
     P.c = (float)((double)softmax_scale * 1.4426950408889634);
-    if (h3::launch_forward(P, i8, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
+    if (h3::launch_forward(P, i8, fp8v, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
+    return H3ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int h3attn_forward(const h3attn_problem* p,
+                   const void* q_prep, const void* k_prep,
+                   const float* q_scales, const float* k_scales,
+                   const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                   void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                   float softmax_scale, void* stream) {
+    return forward_common(p, q_prep, k_prep, q_scales, k_scales, false, v, v_stride_tok, v_stride_head,
+                          nullptr, o, o_stride_tok, o_stride_head, softmax_scale, stream);
+}
+
+int h3attn_forward_fp8v(const h3attn_problem* p,
+                        const void* q_prep, const void* k_prep,
+                        const float* q_scales, const float* k_scales,
+                        const void* v_codes, const float* v_scales,
+                        void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                        float softmax_scale, void* stream) {
+    return forward_common(p, q_prep, k_prep, q_scales, k_scales, true, v_codes, 0, 0, v_scales, o,
+                          o_stride_tok, o_stride_head, softmax_scale, stream);
+}
+
+int h3attn_prep_v_fp8(const h3attn_problem* p, const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                      void* v_codes, float* v_scales, void* stream) {
+    int rc = check_problem(p);
+    if (rc) return rc;
+    if ((rc = check_in_view(v, v_stride_tok, v_stride_head))) return rc;
+    if (!v_codes || !v_scales) return H3ATTN_E_NULL;
+    if (!aligned(v_codes, 16) || !aligned(v_scales, 4)) return H3ATTN_E_ALIGN;
+    const int64_t n = p->n_tokens, h = p->n_heads;
+    const Range vin = view_range(v, n, h, v_stride_tok, v_stride_head, 128, 2);
+    const Range cod = span(v_codes, h3attn_prepped_v_bytes(p));
+    const Range sc = span(v_scales, h3attn_v_scales_bytes(p));
+    if (overlap(cod, vin) || overlap(sc, vin) || overlap(cod, sc)) return H3ATTN_E_ALIAS;
+    h3::PrepVParams P{};
+    P.v = static_cast<const uint16_t*>(v); P.v_st = v_stride_tok; P.v_sh = v_stride_head;
+    P.out = static_cast<uint8_t*>(v_codes); P.scales = v_scales;
+    P.n = (int)n; P.h = (int)h; P.npad = (int)npad_of(p);
+    if (h3::launch_prep_v(P, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
     return H3ATTN_OK;
 }
 

@@ -69,6 +69,15 @@ __device__ __forceinline__ int key_of_row(int rho) {
     return 32 * blk + 16 * (i >> 1) + 8 * hh + 4 * (i & 1) + j;
 }
 
+// The same for the FP8 P V product, whose B operand gives each lane half 32
+// consecutive keys: accumulator element e of block kb in lane half h is key
+// 32h + 16kb + e, so LDS row 32kb + 8i + 4h + j holds key 32h + 16kb + 4i + j.
+__device__ __forceinline__ int key_of_row_f8(int rho) {
+    const int kb = rho >> 5, r = rho & 31;
+    const int i = r >> 3, hh = (r >> 2) & 1, j = r & 3;
+    return 32 * hh + 16 * kb + 4 * i + j;
+}
+
 // One 16-byte-per-lane global -> LDS DMA.  Issued as asm so the compiler does
 // not treat it as an LDS write it must wait for before later LDS reads: the
 // kernel's own vmcnt + barrier protocol orders every buffer's fill before use.
@@ -163,6 +172,11 @@ __device__ __forceinline__ int key_of_elem(int kb, int e, int hh) {
     return 32 * kb + 16 * (e >> 3) + 8 * hh + (e & 7);
 }
 
+template <bool kFp8V>
+__device__ __forceinline__ int key_of(int kb, int e, int hh) {
+    return kFp8V ? 32 * hh + 16 * kb + e : key_of_elem(kb, e, hh);
+}
+
 // acc *= alpha with acc pinned to the accumulation registers (AGPRs): the rare
 // rescale of the running output then never forces O into arch VGPRs.
 __device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
@@ -195,6 +209,7 @@ __device__ __forceinline__ void wait_vmem_upto() {
     else if constexpr (kOutstanding == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     else if constexpr (kOutstanding == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else if constexpr (kOutstanding == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if constexpr (kOutstanding == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -230,11 +245,12 @@ __global__ void __launch_bounds__(256) scores_i8_kernel(ScoreParams P) {
 // ============================================================================
 // The forward kernel (see the file comment).
 // ============================================================================
-template <bool kInt8>
+template <bool kInt8, bool kFp8V>
 struct DmaOffsets8 {
     static constexpr int kRowB = kInt8 ? 128 : 256;   // K' row bytes
     static constexpr int kN = kInt8 ? 1 : 2;          // K' DMA instructions per wave
-    uint32_t k[kN], v[2], vlast[2];
+    static constexpr int kNV = kFp8V ? 1 : 2;         // V DMA instructions per wave
+    uint32_t k[kN], v[kNV], vlast[kNV];
     __device__ __forceinline__ DmaOffsets8(int wave, int lane, int64_t v_st, int last_key0, int n) {
         // each wave moves K' rows 8w..8w+7: 8 (int8) or 4 (bf16) rows per instruction
         constexpr int cpr = kRowB / 16, rpi = 64 / cpr;
@@ -242,26 +258,40 @@ struct DmaOffsets8 {
         for (int r = 0; r < kN; ++r) {
             const int rho = 8 * wave + rpi * r + lane / cpr;
             const int c = (lane % cpr) ^ (rho & (cpr - 1));
-            k[r] = (uint32_t)(key_of_row(rho) * kRowB + c * 16);
+            k[r] = (uint32_t)((kFp8V ? key_of_row_f8(rho) : key_of_row(rho)) * kRowB + c * 16);
         }
-        const uint32_t rs = (uint32_t)(v_st * 2);
+        if constexpr (kFp8V) {
+            // E4M3 V^T tile [128 d][64 keys]: wave w moves d-rows 16w..16w+15;
+            // LDS slot s of row d holds 16-byte chunk s ^ ((d >> 2) & 3)
+            const int d = 16 * wave + (lane >> 2);
+            const int c = (lane & 3) ^ ((d >> 2) & 3);
+            v[0] = vlast[0] = (uint32_t)(d * 64 + c * 16);
+        } else {
+            const uint32_t rs = (uint32_t)(v_st * 2);
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int kappa = 8 * wave + 4 * r + (lane >> 4);
-            const int c = (lane & 15) ^ (4 * (kappa & 3));
-            v[r] = (uint32_t)kappa * rs + c * 16;
-            vlast[r] = (uint32_t)min(kappa, n - 1 - last_key0) * rs + c * 16;
+            for (int r = 0; r < 2; ++r) {
+                const int kappa = 8 * wave + 4 * r + (lane >> 4);
+                const int c = (lane & 15) ^ (4 * (kappa & 3));
+                v[r] = (uint32_t)kappa * rs + c * 16;
+                vlast[r] = (uint32_t)min(kappa, n - 1 - last_key0) * rs + c * 16;
+            }
         }
     }
 };
 
-template <bool kInt8>
+// log2 of the factor applied to P before it is rounded to E4M3: the lazily
+// rescaled P is at most 2^8, times 2^0.8 stays below 448, E4M3's largest
+// finite value, so more of P's range lands on normal E4M3 numbers.  The
+// factor multiplies numerator and denominator alike and cancels.
+constexpr float kPLog2Fp8 = 0.8f;
+
+template <bool kInt8, bool kFp8V>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd8_kernel(FwdParams P) {
-    using D = DmaOffsets8<kInt8>;
+    using D = DmaOffsets8<kInt8, kFp8V>;
     constexpr int kKTileB = kBN * D::kRowB;        // 16 KB (bf16) or 8 KB (int8)
-    constexpr int kVTileB = kBN * 256;             // 16 KB
-    constexpr int kDma8 = D::kN + 2;               // DMA instructions per wave per tile
+    constexpr int kVTileB = kBN * (kFp8V ? 128 : 256);   // 8 KB (E4M3) or 16 KB (bf16)
+    constexpr int kDma8 = D::kN + D::kNV;          // DMA instructions per wave per tile
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * (kKTileB + kVTileB)];
 
     const int vb = (blockIdx.x % kXcds) * P.per_xcd + blockIdx.x / kXcds;
@@ -277,7 +307,8 @@ fwd8_kernel(FwdParams P) {
 
     const uint8_t* qhead = static_cast<const uint8_t*>(P.q) + (int64_t)head * P.npad * D::kRowB;
     const uint8_t* khead = static_cast<const uint8_t*>(P.k) + (int64_t)head * P.npad * D::kRowB;
-    const uint16_t* vhead = P.v + (int64_t)head * P.v_sh;
+    const uint8_t* vhead = kFp8V ? reinterpret_cast<const uint8_t*>(P.v) + (int64_t)head * P.npad * 128
+                                 : reinterpret_cast<const uint8_t*>(P.v + (int64_t)head * P.v_sh);
     auto kbuf = [&](int j) { return lds + (j % kStages) * kKTileB; };
     auto vbuf = [&](int j) { return lds + kStages * kKTileB + (j % kStages) * kVTileB; };
 
@@ -308,21 +339,29 @@ fwd8_kernel(FwdParams P) {
 #pragma unroll
         for (int r = 0; r < D::kN; ++r)
             dma16_buf(kr, dmo.k[r], kbuf(t) + (8 * wave + (kInt8 ? 8 : 4) * r) * D::kRowB);
-        const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kBN * P.v_st);
-        const bool lt = kt == last;
+        if constexpr (kFp8V) {
+            // pad keys of the last tile are zero codes in memory: no clamp
+            const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kVTileB);
+            dma16_buf(vr, dmo.v[0], vbuf(t) + 1024 * wave);
+        } else {
+            const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kBN * P.v_st * 2);
+            const bool lt = kt == last;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) dma16_buf(vr, lt ? dmo.vlast[r] : dmo.v[r], vbuf(t) + (8 * wave + 4 * r) * 256);
+            for (int r = 0; r < 2; ++r)
+                dma16_buf(vr, lt ? dmo.vlast[r] : dmo.v[r], vbuf(t) + (8 * wave + 4 * r) * 256);
+        }
     };
 
     const int r16 = lane & 15, g16 = lane >> 4;
     const int rk = r16 >> 2;
-    const int v_lane_off = (8 * (g16 >> 1) + rk) * 256 + (2 * (g16 & 1) + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1);
+    const int v_lane_off = kFp8V ? n32 * 64 : (8 * (g16 >> 1) + rk) * 256 + (2 * (g16 & 1) + ((r16 & 3) >> 1)) * 16 + 8 * (r16 & 1);
+    const int v_sw = (n32 >> 2) & 3;               // E4M3 V^T chunk swizzle of this lane's rows
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     auto tile = [&](int j, bool masked) {
         fetch(j + 3);
-        // S^T of this wave's 32 queries: S[kb] = keys 32kb..32kb+31
+        // S^T of this wave's 32 queries: S[kb] = LDS rows 32kb..32kb+31
         f32x16 S[2];
         const uint8_t* kb_ = kbuf(j);
         if constexpr (kInt8) {
@@ -369,7 +408,7 @@ fwd8_kernel(FwdParams P) {
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    if (j * kBN + key_of_elem(kb, e, hh) >= n) S[kb][e] = -FLT_MAX;
+                    if (j * kBN + key_of<kFp8V>(kb, e, hh) >= n) S[kb][e] = -FLT_MAX;
         }
         float mx = S[0][0];
 #pragma unroll
@@ -385,32 +424,67 @@ fwd8_kernel(FwdParams P) {
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) scale_acc(O[cc], alpha);
         }
-        bf16x8 Pb[2][2];
-        float rs[2] = {0.f, 0.f};
+        if constexpr (kFp8V) {
+            // P' = 2^0.8 * P rounded to E4M3, 32 consecutive keys per lane half;
+            // the row sum adds the fp32 P' before rounding
+            const float mb = m - kPLog2Fp8;
+            i32x8 Pf;
+            float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                u32x4 w;
+                for (int w4 = 0; w4 < 4; ++w4) {
+                    float x[4];
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int e = 8 * s + 2 * ii;
-                    float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -m));
-                    float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], coef, -m));
-                    if (masked) {
-                        if (j * kBN + key_of_elem(kb, e, hh) >= n) x0 = 0.f;
-                        if (j * kBN + key_of_elem(kb, e + 1, hh) >= n) x1 = 0.f;
+                    for (int u = 0; u < 4; ++u) {
+                        const int e = 4 * w4 + u;
+                        x[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mb));
+                        if (masked && j * kBN + key_of<true>(kb, e, hh) >= n) x[u] = 0.f;
+                        rs[u] += x[u];
                     }
-                    const f32x2 f = {x0, x1};
-                    const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
-                    rs[s] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs[s], false);
-                    w[ii] = __builtin_bit_cast(uint32_t, b);
+                    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                    wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wd, true);
+                    Pf[4 * kb + w4] = wd;
                 }
-                Pb[kb][s] = __builtin_bit_cast(bf16x8, w);
+            l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+            // O^T += V^T P'^T: lane (n32, hh) reads d-row 32cc + n32, keys 32hh..32hh+31
+            const uint8_t* vb_ = vbuf(j) + v_lane_off;
+            const int s0 = ((2 * hh) ^ v_sw) * 16, s1 = ((2 * hh + 1) ^ v_sw) * 16;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const i32x4 lo = *reinterpret_cast<const i32x4*>(vb_ + 32 * 64 * cc + s0);
+                const i32x4 hi = *reinterpret_cast<const i32x4*>(vb_ + 32 * 64 * cc + s1);
+                const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                // formats 0/0: E4M3 A and B; unit E8M0 block scales (127 = 2^0)
+                O[cc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, Pf, O[cc], 0, 0, 0, 0x7f7f7f7f, 0,
+                                                                        0x7f7f7f7f);
             }
-        l += rs[0] + rs[1];
-        // O^T += V^T P^T
-        {
+        } else {
+            bf16x8 Pb[2][2];
+            float rs[2] = {0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    u32x4 w;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const int e = 8 * s + 2 * ii;
+                        float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -m));
+                        float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], coef, -m));
+                        if (masked) {
+                            if (j * kBN + key_of_elem(kb, e, hh) >= n) x0 = 0.f;
+                            if (j * kBN + key_of_elem(kb, e + 1, hh) >= n) x1 = 0.f;
+                        }
+                        const f32x2 f = {x0, x1};
+                        const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+                        rs[s] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs[s], false);
+                        w[ii] = __builtin_bit_cast(uint32_t, b);
+                    }
+                    Pb[kb][s] = __builtin_bit_cast(bf16x8, w);
+                }
+            l += rs[0] + rs[1];
+            // O^T += V^T P^T
             const uint8_t* vb_ = vbuf(j);
             typedef short i16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
@@ -444,30 +518,43 @@ fwd8_kernel(FwdParams P) {
     for (int j = 0; j < last; ++j) tile(j, false);
     tile(last, ragged);
     wait_vmem_all();
+    // O is complete here in every lane.  A matrix-core product reads the
+    // operands (and the E4M3 path's per-lane scale registers) of all 64 lanes,
+    // so none may move into the store branch below, where the lanes of rows
+    // >= N are switched off: this empty statement consumes O before it.
+    asm volatile("" ::"a"(O[0]), "a"(O[1]), "a"(O[2]), "a"(O[3]));
 
     const float lt = l + __shfl_xor(l, 32);
     const float inv = 1.0f / lt;
     const int qrow = q0 + n32;
     if (qrow < n) {
         uint16_t* orow = P.o + (int64_t)qrow * P.o_st + (int64_t)head * P.o_sh;
+        const float* vsh = kFp8V ? P.vs + (int64_t)head * 128 : nullptr;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const u32x2 w = {pack_bf16x2(O[cc][4 * i] * inv, O[cc][4 * i + 1] * inv),
-                                 pack_bf16x2(O[cc][4 * i + 2] * inv, O[cc][4 * i + 3] * inv)};
-                st8(orow + 32 * cc + 8 * i + 4 * hh, w);
+                const int d0 = 32 * cc + 8 * i + 4 * hh;
+                float f[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) f[u] = kFp8V ? O[cc][4 * i + u] * (vsh[d0 + u] * inv) : O[cc][4 * i + u] * inv;
+                const u32x2 w = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+                st8(orow + d0, w);
             }
     }
 }
 
-hipError_t launch_forward(const FwdParams& P, bool int8, hipStream_t stream) {
+hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
-    dim3 grid(kXcds * P.per_xcd), block(256);
-    if (int8)
-        hipLaunchKernelGGL(fwd8_kernel<true>, grid, dim3(512), 0, stream, P);
+    const dim3 grid(kXcds * P.per_xcd), block(512);
+    if (int8 && fp8v)
+        hipLaunchKernelGGL((fwd8_kernel<true, true>), grid, block, 0, stream, P);
+    else if (int8)
+        hipLaunchKernelGGL((fwd8_kernel<true, false>), grid, block, 0, stream, P);
+    else if (fp8v)
+        hipLaunchKernelGGL((fwd8_kernel<false, true>), grid, block, 0, stream, P);
     else
-        hipLaunchKernelGGL(fwd8_kernel<false>, grid, dim3(512), 0, stream, P);
+        hipLaunchKernelGGL((fwd8_kernel<false, false>), grid, block, 0, stream, P);
     return hipGetLastError();
 }
 

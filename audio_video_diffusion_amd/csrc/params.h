@@ -18,12 +18,20 @@ struct PrepParams {
     int sec0, sec1, sec2;
 };
 
+struct PrepVParams {
+    const uint16_t* v; int64_t v_st, v_sh;      // bf16 NHD view (element strides)
+    uint8_t* out;                                // [H][npad/64][128][64] E4M3 codes
+    float* scales;                               // [H][128]: absmax, then scale
+    int n, h, npad;
+};
+
 struct FwdParams {
     const void* q;          // [H][npad][128] bf16 or int8
     const void* k;
     const float* qs;        // [H][nblk] (int8 only)
     const float* ks;
-    const uint16_t* v; int64_t v_st, v_sh;
+    const uint16_t* v; int64_t v_st, v_sh;      // bf16 V view, or E4M3 V tiles (fp8v)
+    const float* vs;                             // [H][128] V channel scales (fp8v only)
     uint16_t* o; int64_t o_st, o_sh;
     int n, h, npad, nblk;
     int qtiles;             // ceil(N / 256)
@@ -41,7 +49,8 @@ struct ScoreParams {
 };
 
 hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream);
-hipError_t launch_forward(const FwdParams& P, bool int8, hipStream_t stream);
+hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t stream);
+hipError_t launch_prep_v(const PrepVParams& P, hipStream_t stream);
 hipError_t launch_scores_i8(const ScoreParams& P, hipStream_t stream);
 
 }  // namespace h3

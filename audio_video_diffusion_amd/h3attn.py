@@ -8,6 +8,8 @@ The calls mirror ``include/h3attn.h``:
 
 * :func:`prep`      - Q/K RMSNorm + 3-axis split-half RoPE -> head-major Q'/K'
 * :func:`forward`   - softmax(Q' K'^T * scale) V over the packed sequence
+* :func:`prep_v_fp8` - V -> E4M3 codes (d-major 64-key tiles) + fp32 channel scales
+* :func:`forward_fp8v` - :func:`forward` with the P V product on FP8 matrix cores
 * :func:`debug_scores_i32` - exact int32 Q'K'^T window of the int8 format
 """
 from __future__ import annotations
@@ -20,7 +22,7 @@ LIB_PATH = os.path.join(PKG, "libh3attn.so")
 
 QK_BF16 = 0
 QK_I8_BLK64 = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_UNSUPPORTED", -4: "E_ALIGN",
           -5: "E_ALIAS", -6: "E_HIP"}
@@ -80,9 +82,13 @@ def _load():
         "h3attn_padded_tokens": (i64, [pp]),
         "h3attn_prepped_qk_bytes": (ctypes.c_size_t, [pp]),
         "h3attn_scales_bytes": (ctypes.c_size_t, [pp]),
+        "h3attn_prepped_v_bytes": (ctypes.c_size_t, [pp]),
+        "h3attn_v_scales_bytes": (ctypes.c_size_t, [pp]),
         "h3attn_prep": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, i64, vp, vp, i64, vp,
                                        vp, vp, vp, vp, vp]),
         "h3attn_forward": (ctypes.c_int, [pp, vp, vp, vp, vp, vp, i64, i64, vp, i64, i64, f32, vp]),
+        "h3attn_prep_v_fp8": (ctypes.c_int, [pp, vp, i64, i64, vp, vp, vp]),
+        "h3attn_forward_fp8v": (ctypes.c_int, [pp, vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, vp]),
         "h3attn_debug_scores_i32": (ctypes.c_int, [pp, vp, vp, i32, i32, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -109,6 +115,14 @@ def prepped_qk_bytes(p: Problem) -> int:
 
 def scales_bytes(p: Problem) -> int:
     return _lib.h3attn_scales_bytes(ctypes.byref(p))
+
+
+def prepped_v_bytes(p: Problem) -> int:
+    return _lib.h3attn_prepped_v_bytes(ctypes.byref(p))
+
+
+def v_scales_bytes(p: Problem) -> int:
+    return _lib.h3attn_v_scales_bytes(ctypes.byref(p))
 
 
 # ---------------------------------------------------------------------------
@@ -170,6 +184,33 @@ def forward(p: Problem, q_prep, k_prep, v, o, softmax_scale: float, q_scales=Non
                              _stream(stream))
     if rc:
         raise H3AttnError(rc, "h3attn_forward")
+
+
+def alloc_v_fp8(p: Problem, device="cuda"):
+    """Caller-side buffers for :func:`prep_v_fp8`: (codes uint8 [H, N_pad/64, 128, 64], scales fp32 [H, 128])."""
+    import torch
+    npad = padded_tokens(p)
+    codes = torch.empty((p.n_heads, npad // 64, p.head_dim, 64), dtype=torch.uint8, device=device)
+    return codes, torch.empty((p.n_heads, p.head_dim), dtype=torch.float32, device=device)
+
+
+def prep_v_fp8(p: Problem, v, v_codes, v_scales, stream=None):
+    """``h3attn_prep_v_fp8`` on torch tensors (v bf16 [N,H,d] view)."""
+    vp, vst, vsh = _nhd(v, "v")
+    rc = _lib.h3attn_prep_v_fp8(ctypes.byref(p), vp, vst, vsh, _ptr(v_codes), _ptr(v_scales), _stream(stream))
+    if rc:
+        raise H3AttnError(rc, "h3attn_prep_v_fp8")
+
+
+def forward_fp8v(p: Problem, q_prep, k_prep, v_codes, v_scales, o, softmax_scale: float, q_scales=None,
+                 k_scales=None, stream=None):
+    """``h3attn_forward_fp8v`` on torch tensors (o bf16 [N,H,d] view)."""
+    op, ost, osh = _nhd(o, "o")
+    rc = _lib.h3attn_forward_fp8v(ctypes.byref(p), _ptr(q_prep), _ptr(k_prep), _ptr(q_scales),
+                                  _ptr(k_scales), _ptr(v_codes), _ptr(v_scales), op, ost, osh,
+                                  float(softmax_scale), _stream(stream))
+    if rc:
+        raise H3AttnError(rc, "h3attn_forward_fp8v")
 
 
 def debug_scores_i32(p: Problem, q_codes, k_codes, head: int, row0: int, nrows: int, col0: int,

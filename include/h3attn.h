@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 1
+#define H3ATTN_ABI_VERSION 2
 
 typedef enum {
     H3ATTN_OK = 0,
@@ -88,6 +88,12 @@ size_t h3attn_prepped_qk_bytes(const h3attn_problem* p);
 /* Bytes of ONE scale array (Q' or K') in int8 format: H * ceil(N/64) * 4,
  * fp32 [H][ceil(N/64)]; 0 in bf16 format or for an invalid descriptor. */
 size_t h3attn_scales_bytes(const h3attn_problem* p);
+
+/* Bytes of the E4M3 V tiles that h3attn_prep_v_fp8 writes: H * N_pad * 128. */
+size_t h3attn_prepped_v_bytes(const h3attn_problem* p);
+
+/* Bytes of the fp32 V channel scales that h3attn_prep_v_fp8 writes: H * 128 * 4. */
+size_t h3attn_v_scales_bytes(const h3attn_problem* p);
 
 /*
  * h3attn_prep - per-head RMSNorm, then 3-axis split-half RoPE, of Q and K.
@@ -170,6 +176,53 @@ int h3attn_forward(const h3attn_problem* p,
                    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
                    void* o, int64_t o_stride_tok, int64_t o_stride_head,
                    float softmax_scale, void* stream);
+
+/*
+ * h3attn_prep_v_fp8 - V to OCP E4M3 with one fp32 scale per (head, channel),
+ * the V preparation of the FP8 P V path ("H3 Runtime Current State", Owned
+ * Performance Kernels: V transpose/pad and V scale/FP8 quantization; the owned
+ * V-preparation study emits E4M3 V plus FP32 per-channel scales).
+ *
+ * For every head h and channel c, over all N tokens:
+ *   a = max_n |V[n,h,c]|, s = a / 448, inv = 448 / a   (fp32, nearest-even),
+ *   code = E4M3(clamp(V[n,h,c] * inv, -448, 448))       (nearest, ties to even;
+ *                                                        subnormals kept),
+ *   a == 0 gives s = 0 and zero codes.
+ * v:        bf16 view [N][H][128], strides as for q in h3attn_prep.
+ * v_codes:  h3attn_prepped_v_bytes(p) bytes, 16-byte aligned.  Per head,
+ *           N_pad/64 tiles of 64 keys; each tile d-major: byte
+ *           v_codes[((h*N_pad/64 + m/64)*128 + c)*64 + m%64] is the code of
+ *           V[m,h,c]; keys m >= N are 0.
+ * v_scales: fp32 [H][128], 4-byte aligned: s per (head, channel).
+ * Outputs must not overlap v or each other.  The descriptor's qk_format is
+ * ignored.  Four kernels on `stream`; nothing is allocated.
+ * Errors: as for h3attn_prep.
+ */
+int h3attn_prep_v_fp8(const h3attn_problem* p,
+                      const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                      void* v_codes, float* v_scales, void* stream);
+
+/*
+ * h3attn_forward_fp8v - h3attn_forward with the P V product on the FP8 matrix
+ * cores: V comes as E4M3 codes with per-channel scales (h3attn_prep_v_fp8) and
+ * the probabilities are rounded to E4M3 for the product (the FP8-PV half of the
+ * SageAttention2 path, "H3 Runtime Current State", Owned Performance Kernels:
+ * INT8 QK and FP8 PV).  Q'/K' in either qk_format, as for h3attn_forward.
+ *   O[n,h,c] = s[h,c] * sum_m E4M3(a * P[n,m]) code[m,h,c] / sum_m a * P[n,m]
+ * where P[n,m] = 2^(log2(e) * scale * (S[n,m] - M)) are the fp32 softmax
+ * numerators against a running row maximum M that the kernel raises only when
+ * a score exceeds it by more than 8 / (log2(e) * scale), so P <= 2^8, and
+ * a = 2^0.8 keeps a * P below 448; a cancels in the quotient.  The rounding
+ * is nearest-even with subnormals, as in h3attn_prep_v_fp8.
+ * v_codes/v_scales: as written by h3attn_prep_v_fp8 for the same descriptor.
+ * Other arguments and errors: as for h3attn_forward.
+ */
+int h3attn_forward_fp8v(const h3attn_problem* p,
+                        const void* q_prep, const void* k_prep,
+                        const float* q_scales, const float* k_scales,
+                        const void* v_codes, const float* v_scales,
+                        void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                        float softmax_scale, void* stream);
 
 /*
  * h3attn_debug_scores_i32 - test hook for the int8 format: the exact int32

@@ -20,6 +20,11 @@ pages "H3 Runtime Current State" and "H3 Blackwell Runtime Plan"):
    block per head, and exact int32 Q K^T accumulation (the int8-QK step of the
    SageAttention2 path: "H3 Runtime Current State", Owned Performance Kernels,
    Q quantization and K quantization).
+5. Optional FP8 (OCP E4M3) V with one fp32 scale per channel per head, the
+   FP8-PV step of the same path ("H3 Runtime Current State", Owned Performance
+   Kernels: V scale/FP8 quantization; the V-preparation study emits E4M3 V plus
+   FP32 per-channel scales).  The GPU also rounds P to E4M3 inside its P V
+   product; the oracle keeps P exact, as it keeps P exact against bf16.
 
 All floating point is fp64 except where the method fixes fp32 (the int8
 quantiser, whose rounding decisions must match bit for bit).
@@ -35,6 +40,10 @@ the design notes of the repository):
 * Int8: round-half-even, symmetric +-127, blocks of 64 tokens from token 0
   with a partial last block, scale = fl32(absmax/127), codes =
   rint(fl32(x * fl32(127/absmax))), an all-zero block has scale 0 and codes 0.
+* FP8 V: per head and channel over all N tokens, scale = fl32(absmax/448),
+  value = clamp(fl32(v * fl32(448/absmax)), -448, 448), rounded to the nearest
+  E4M3 value (ties to even mantissa, subnormals kept); an all-zero channel has
+  scale 0 and codes 0.  448 is the largest finite E4M3 value.
 """
 from __future__ import annotations
 
@@ -45,6 +54,7 @@ __all__ = [
     "rmsnorm", "rope_layout", "rope", "prep", "prep_head",
     "softmax_rows", "attention", "attention_head", "attention_rows_head",
     "quantize_i8", "scores_i32", "attention_i8_rows_head",
+    "e4m3_bits", "e4m3_bits_to_f64", "quantize_v_fp8", "dequantize_v_fp8",
 ]
 
 
@@ -253,3 +263,93 @@ def attention_i8_rows_head(rows: np.ndarray, codes_q: np.ndarray, scales_q: np.n
         s = s_int * sq[:, None] * sk[None, :] * scale
         out[r0:r0 + qblock] = softmax_rows(s) @ v
     return out
+
+
+# ----------------------------------------------------------------------------
+# 5. FP8 (OCP E4M3) V with per-channel fp32 scales
+# ----------------------------------------------------------------------------
+# E4M3 (OCP 8-bit floating point, "fn" variant): 1 sign bit, 4 exponent bits
+# with bias 7, 3 mantissa bits; no infinities; S.1111.111 is NaN; the largest
+# finite value is 1.75 * 2^8 = 448; normals start at 2^-6; subnormals are
+# m * 2^-9 for m = 1..7.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Encode finite values with |x| <= 448 as E4M3 bytes, nearest value, ties to even.
+
+    Works per element in float64 (every step below is exact in float64 for
+    float32 inputs): pick the binade, scale the magnitude to units of the
+    binade's spacing, round half to even with numpy's rint, and carry a
+    mantissa overflow into the next binade.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(~np.isfinite(x)) or np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("e4m3_bits expects finite values with |x| <= 448")
+    sign = (np.signbit(x)).astype(np.uint8) << 7
+    a = np.abs(x)
+    out = np.zeros(x.shape, dtype=np.uint8)
+    # exponent of the binade (values below 2^-6 use the subnormal spacing 2^-9)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0))).astype(np.int64)
+    e = np.clip(e, -6, 8)
+    # log2 of an exact power of two can be off by one in floating point: fix up
+    e = np.where((a > 0) & (a < np.ldexp(1.0, e)) & (e > -6), e - 1, e)
+    e = np.where((a >= np.ldexp(1.0, e + 1)) & (e < 8), e + 1, e)
+    sub = a < 2.0 ** -6
+    # mantissa in units of 2^(e-3) (normal) or 2^-9 (subnormal)
+    unit = np.where(sub, 2.0 ** -9, np.ldexp(1.0, e - 3))
+    q = np.rint(a / unit)                      # exact division by a power of two
+    # normal: q in [8, 16]; 16 carries into the next binade
+    carry = (~sub) & (q >= 16)
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 8, q)
+    # subnormal rounding up to 8 units is the smallest normal 2^-6 (exponent field 1)
+    mant = np.where(sub, np.where(q >= 8, 0, q), q - 8).astype(np.int64)
+    expf = np.where(sub, np.where(q >= 8, 1, 0), e + 7).astype(np.int64)
+    out = (sign | ((expf << 3) | mant).astype(np.uint8)).astype(np.uint8)
+    return out
+
+
+def e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode E4M3 bytes (finite codes) to float64 exactly."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    expf = (b >> 3) & 0xF
+    mant = b & 0x7
+    if np.any((expf == 0xF) & (mant == 0x7)):
+        raise ValueError("NaN code")
+    val = np.where(expf == 0, mant * 2.0 ** -9, np.ldexp(1.0 + mant / 8.0, expf - 7))
+    return sign * val
+
+
+def quantize_v_fp8(v: np.ndarray):
+    """Quantise one head's V (float32 [N, d]) to E4M3 with one fp32 scale per channel.
+
+    Per channel c (a single float32 operation per step, rounded to nearest even):
+    a = max_n |v[n, c]| (exact), s = a / 448, inv = 448 / a,
+    x = clamp(v * inv, -448, 448), code = E4M3 nearest (ties to even).
+    a == 0 gives s = 0 and zero codes.  Returns (codes uint8 [N, d], scales float32 [d]).
+    """
+    v = np.asarray(v)
+    if v.dtype != np.float32:
+        raise TypeError("quantize_v_fp8 expects float32 input")
+    n, d = v.shape
+    codes = np.zeros((n, d), dtype=np.uint8)
+    scales = np.zeros(d, dtype=np.float32)
+    f448 = np.float32(E4M3_MAX)
+    for c in range(d):
+        col = v[:, c]
+        a = np.float32(np.max(np.abs(col))) if n else np.float32(0)
+        if a == 0:
+            continue
+        scales[c] = a / f448
+        inv = f448 / a
+        x = np.clip((col * inv).astype(np.float32), -f448, f448)
+        codes[:, c] = e4m3_bits(x)
+    return codes, scales
+
+
+def dequantize_v_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The V the FP8 P V product multiplies: code value times channel scale (float64)."""
+    return e4m3_bits_to_f64(codes) * scales.astype(np.float64)[None, :]

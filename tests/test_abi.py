@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 1
+    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 2
     for s in (0, -1, -2, -3, -4, -5, -6, 7):
         assert A.lib.h3attn_status_string(s)
 
@@ -55,6 +55,10 @@ def test_sizes():
     assert A.padded_tokens(A.problem(1, 1)) == 256
     assert A.padded_tokens(A.problem(0, 1)) == 0
     assert A.prepped_qk_bytes(A.problem(10, 1, head_dim=64)) == 0
+    assert A.prepped_v_bytes(p) == 24 * 129536 * 128
+    assert A.v_scales_bytes(p) == 24 * 128 * 4
+    assert A.prepped_v_bytes(p8) == 24 * 246528 * 128
+    assert A.prepped_v_bytes(A.problem(10, 1, head_dim=64)) == 0
 
 
 def prep(p, q=F, qst=384, qsh=128, k=G, kst=384, ksh=128, gq=H, gk=H + 256, gsh=0, pos=I,
@@ -137,6 +141,44 @@ def test_forward_checks():
     p8 = A.problem(1000, 3, A.QK_I8_BLK64)
     assert fwd(p8) == -1
     assert fwd(p8, qs=K, ks=K + 4096, o=K + 16) == -5
+
+
+def prep_v(p, v=F, vst=384, vsh=128, codes=G, scales=H):
+    return A.lib.h3attn_prep_v_fp8(ctypes.byref(p), v, vst, vsh, codes, scales, None)
+
+
+def fwd8v(p, q=F, k=G, qs=None, ks=None, codes=H, vs=J, o=I, ost=384, osh=128, scale=0.088):
+    return A.lib.h3attn_forward_fp8v(ctypes.byref(p), q, k, qs, ks, codes, vs, o, ost, osh, scale, None)
+
+
+def test_prep_v_fp8_checks():
+    p = A.problem(1000, 3)
+    assert prep_v(A.problem(1000, 3, head_dim=64)) == -3
+    assert prep_v(p, v=None) == -1
+    assert prep_v(p, codes=None) == -1
+    assert prep_v(p, scales=None) == -1
+    assert prep_v(p, v=F + 2) == -4
+    assert prep_v(p, codes=G + 8) == -4
+    assert prep_v(p, scales=H + 2) == -4
+    assert prep_v(p, vst=100) == -4
+    assert prep_v(p, codes=F + 384 * 10) == -5                 # codes on top of v
+    assert prep_v(p, scales=F + 64) == -5                      # scales inside v
+    assert prep_v(p, scales=G + A.prepped_v_bytes(p) - 4) == -5   # scales overlap the codes' end
+
+
+def test_forward_fp8v_checks():
+    p = A.problem(1000, 3)
+    assert fwd8v(p, codes=None) == -1
+    assert fwd8v(p, vs=None) == -1
+    assert fwd8v(p, q=None) == -1
+    assert fwd8v(p, codes=H + 8) == -4
+    assert fwd8v(p, vs=J + 2) == -4
+    assert fwd8v(p, scale=0.0) == -2
+    assert fwd8v(p, qs=K) == -2                                # scales in bf16 format
+    assert fwd8v(p, o=H + 4096) == -5                          # output inside the codes
+    assert fwd8v(p, o=J - 64) == -5                            # output over the V scales
+    p8 = A.problem(1000, 3, A.QK_I8_BLK64)
+    assert fwd8v(p8) == -1
 
 
 def test_debug_scores_checks():

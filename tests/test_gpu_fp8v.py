@@ -1,0 +1,342 @@
+"""GPU parity of the FP8 P V path: V staged as E4M3 codes with per-channel
+scales, and the forward whose P V product runs on the FP8 matrix cores.
+
+* the staged codes and scales are compared bit for bit with the oracle's
+  quantiser (boundary lengths, ragged tails, strided V views);
+* the forward is compared with the oracle's exact softmax over the same Q'/K'
+  and the dequantised V.  The only approximation left is the rounding of the
+  softmax numerators to E4M3, bounded per output element from the format
+  (relative 2^-4 for normal values, absolute 2^-10 below 2^-6), plus a
+  statistical gate: the relative L2 error of nearest rounding to 3 mantissa
+  bits is about 2.7% for normal values and grows for the subnormal tail of
+  diffuse rows (simulated 2.3% to 4.2% over score spreads 1 to 2);
+* closed forms at the full 129,410-token size pin the numerator scale 2^0.8
+  and the fp32 denominator.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from audio_video_diffusion_amd import h3attn as A
+from audio_video_diffusion_amd import workloads as W
+
+from gpu_util import SCALE, errors, f64, problem_for, run_prep
+
+pytestmark = pytest.mark.gpu
+
+ALPHA = 2.0 ** 0.8          # numerator factor before E4M3 rounding (cancels in the quotient)
+REL_L2_FP8 = 5e-2           # stage gate (see the module docstring)
+REL_L2_FP8_E2E = 8e-2       # against fp64 with the unquantised V: P and V rounding together
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu] {request.node.name}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def run_prep_v(p, v):
+    codes, scales = A.alloc_v_fp8(p)
+    A.prep_v_fp8(p, v, codes, scales)
+    return codes, scales
+
+
+def codes_nhd(codes, n):
+    """[H, N_pad/64, 128, 64] tiles -> uint8 numpy [H, N, 128]."""
+    h = codes.shape[0]
+    return codes.permute(0, 1, 3, 2).reshape(h, -1, 128)[:, :n].cpu().numpy()
+
+
+def run_fwd8v(p, q_out, k_out, codes, scales, n, h, qs=None, ks=None):
+    o = torch.empty((n, h, 128), dtype=torch.bfloat16, device="cuda")
+    A.forward_fp8v(p, q_out, k_out, codes, scales, o, SCALE, qs, ks)
+    return o
+
+
+def stage_rows(s, v_hat):
+    """Exact softmax rows of the scores ``s`` [r, N] (already times the softmax
+    scale) against ``v_hat`` [N, d], and the E4M3 rounding bound per element.
+
+    With Z = sum_m exp(s_m - max s), the kernel's denominator is at least
+    2^0.8 * Z, and rounding numerator m changes it by at most
+    max(2^-4 * its value, 2^-10); summed against |v| this bounds the output error.
+    """
+    smax = s.max(axis=1, keepdims=True)
+    e = np.exp(s - smax)
+    z = e.sum(axis=1, keepdims=True)
+    r = e / z
+    av = np.abs(v_hat)
+    ref = r @ v_hat
+    bound = 2.0 ** -4 * (r @ av) + 2.0 ** -10 / (ALPHA * z) * av.sum(axis=0)[None, :]
+    return ref, bound
+
+
+def check_fp8(got, ref, bound, what, rel_l2=REL_L2_FP8):
+    mx, mn, rel = errors(got, ref)
+    slack = 2.0 ** -8 * (np.abs(ref) + bound) + 1e-3
+    over = np.abs(got - ref) - (bound + slack)
+    print(f"    {what}: max_abs={mx:.3e} mean_abs={mn:.3e} rel_l2={rel:.3e} "
+          f"worst bound use={np.max(np.abs(got - ref) / (bound + slack)):.3f}", flush=True)
+    assert np.all(np.isfinite(got)), what
+    assert np.all(over <= 0), (what, float(over.max()))
+    assert rel <= rel_l2, (what, rel)
+
+
+def v_hat_of(inp_v_bits_head):
+    c, s = O.quantize_v_fp8(O.bf16_bits_to_f64(inp_v_bits_head).astype(np.float32))
+    return O.dequantize_v_fp8(c, s)
+
+
+# ---------------------------------------------------------------------------
+# V staging: bit-exact codes and scales
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,n,h", [(0, None, None), (71, 1, 1), (72, 63, 2), (73, 64, 1), (74, 65, 2),
+                                     (75, 1000, 3), (76, 4099, 2)])
+def test_prep_v_fp8_codes_and_scales_bit_exact(cfg, n, h):
+    wl = W.WORKLOADS[0] if n is None else W.ragged_workload(n, h)
+    inp = W.make_inputs(cfg, wl)
+    p = problem_for(wl)
+    print(f"    N={wl.n_tokens} H={wl.heads}", flush=True)
+    v = W.bits_to_torch(inp.v)
+    codes, scales = run_prep_v(p, v)
+    npad = A.padded_tokens(p)
+    got_all = codes.permute(0, 1, 3, 2).reshape(wl.heads, npad, 128).cpu().numpy()
+    sc = scales.cpu().numpy()
+    for hh in range(wl.heads):
+        c_ref, s_ref = O.quantize_v_fp8(O.bf16_bits_to_f64(inp.v[:, hh, :]).astype(np.float32))
+        assert np.array_equal(sc[hh], s_ref), hh
+        assert np.array_equal(got_all[hh, :wl.n_tokens], c_ref), hh
+        assert np.all(got_all[hh, wl.n_tokens:] == 0)
+
+
+def test_prep_v_fp8_strided_view_zero_channel_and_reuse():
+    # V as a strided view of an interleaved [N, 3, H, d] buffer; one channel all
+    # zero (scale 0, codes 0); the same buffers reused for a second, smaller call
+    n, h = 777, 3
+    g = torch.Generator(device="cuda").manual_seed(9)
+    qkv = (torch.randn((n, 3, h, 128), generator=g, device="cuda") * 3).to(torch.bfloat16)
+    qkv[:, 2, 1, 5] = 0
+    v = qkv[:, 2]
+    p = A.problem(n, h)
+    codes, scales = run_prep_v(p, v)
+    vb = W.torch_to_bits(v)
+    for hh in range(h):
+        c_ref, s_ref = O.quantize_v_fp8(O.bf16_bits_to_f64(vb[:, hh, :]).astype(np.float32))
+        assert np.array_equal(scales[hh].cpu().numpy(), s_ref)
+        assert np.array_equal(codes_nhd(codes, n)[hh], c_ref)
+    assert scales[1, 5].item() == 0.0
+    # second call, fewer tokens, into the same (larger) buffers: fully rewritten
+    p2 = A.problem(300, h)
+    A.prep_v_fp8(p2, v[:300], codes, scales)
+    vb2 = W.torch_to_bits(v[:300])
+    npad2 = A.padded_tokens(p2)
+    got2 = codes.view(-1)[:h * npad2 * 128].view(h, npad2 // 64, 128, 64)
+    for hh in range(h):
+        c_ref, s_ref = O.quantize_v_fp8(O.bf16_bits_to_f64(vb2[:, hh, :]).astype(np.float32))
+        assert np.array_equal(scales[hh].cpu().numpy(), s_ref)
+        assert np.array_equal(codes_nhd(got2, 300)[hh], c_ref)
+
+
+# ---------------------------------------------------------------------------
+# forward: small cases, every output element
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [None, 1, 2, 63, 64, 65, 129, 257, 1000, 4099])
+@pytest.mark.parametrize("int8", [False, True])
+def test_forward_fp8v_matches_oracle(n, int8):
+    wl = W.WORKLOADS[0] if n is None else W.ragged_workload(n, 2)
+    inp = W.make_inputs(200 + (n or 0) + (1 if int8 else 0), wl)
+    N, H = wl.n_tokens, wl.heads
+    print(f"    N={N} H={H} int8={int8}", flush=True)
+    dev = W.device_inputs(inp)
+    p16 = problem_for(wl)
+    q16, k16, _, _ = run_prep(p16, dev)
+    codes, vsc = run_prep_v(p16, dev["v"])
+    if int8:
+        p8 = problem_for(wl, int8=True)
+        q8, k8, qs, ks = run_prep(p8, dev)
+        o = run_fwd8v(p8, q8, k8, codes, vsc, N, H, qs, ks)
+    else:
+        o = run_fwd8v(p16, q16, k16, codes, vsc, N, H)
+    got = f64(o)
+    refs, bounds, gots = [], [], []
+    for hh in range(H):
+        if int8:
+            cq, cs = q8[hh, :N].cpu().numpy(), qs[hh].cpu().numpy().astype(np.float64)
+            ckk, ksc = k8[hh, :N].cpu().numpy(), ks[hh].cpu().numpy().astype(np.float64)
+            blk = np.arange(N) // 64
+            s = O.scores_i32(cq, ckk).astype(np.float64) * cs[blk][:, None] * ksc[blk][None, :] * SCALE
+        else:
+            qv, kv = f64(q16)[hh, :N], f64(k16)[hh, :N]
+            s = (qv @ kv.T) * SCALE
+        ref, bound = stage_rows(s, v_hat_of(inp.v[:, hh, :]))
+        refs.append(ref)
+        bounds.append(bound)
+        gots.append(got[:, hh, :])
+    check_fp8(np.stack(gots), np.stack(refs), np.stack(bounds), what="fp8v stage")
+    # whole path against the fp64 oracle with the unquantised V
+    qp = O.prep(inp.q, inp.gamma_q, inp.pos, W.ROPE_SECTIONS, W.ROPE_THETA, W.RMS_EPS)
+    kp = O.prep(inp.k, inp.gamma_k, inp.pos, W.ROPE_SECTIONS, W.ROPE_THETA, W.RMS_EPS)
+    ref64 = O.attention(qp, kp, O.bf16_bits_to_f64(inp.v), SCALE)
+    mx, mn, rel = errors(got, ref64)
+    print(f"    fp8v vs fp64: max_abs={mx:.3e} mean_abs={mn:.3e} rel_l2={rel:.3e}", flush=True)
+    assert rel <= REL_L2_FP8_E2E, rel
+
+
+def test_forward_fp8v_sharp_softmax_rescaling():
+    # gamma x 4: logits ~16x sharper, the running max moves in many steps and
+    # the numerators span the whole E4M3 range up to 2^8 * 2^0.8
+    wl = W.ragged_workload(3000, 2)
+    inp = W.make_inputs(21, wl)
+    four = O.f32_to_bf16_bits((O.bf16_bits_to_f64(inp.gamma_q) * 4).astype(np.float32))
+    inp.gamma_q = four
+    inp.gamma_k = four
+    p = problem_for(wl)
+    dev = W.device_inputs(inp)
+    q16, k16, _, _ = run_prep(p, dev)
+    codes, vsc = run_prep_v(p, dev["v"])
+    o = run_fwd8v(p, q16, k16, codes, vsc, wl.n_tokens, wl.heads)
+    got = f64(o)
+    refs, bounds = [], []
+    for hh in range(wl.heads):
+        qv, kv = f64(q16)[hh, :wl.n_tokens], f64(k16)[hh, :wl.n_tokens]
+        ref, bound = stage_rows((qv @ kv.T) * SCALE, v_hat_of(inp.v[:, hh, :]))
+        refs.append(ref)
+        bounds.append(bound)
+    check_fp8(got.transpose(1, 0, 2), np.stack(refs), np.stack(bounds), what="fp8v sharp stage")
+
+
+def test_forward_fp8v_is_deterministic():
+    wl = W.ragged_workload(5000, 3)
+    inp = W.make_inputs(22, wl)
+    p = problem_for(wl)
+    dev = W.device_inputs(inp)
+    q16, k16, _, _ = run_prep(p, dev)
+    codes, vsc = run_prep_v(p, dev["v"])
+    a = run_fwd8v(p, q16, k16, codes, vsc, wl.n_tokens, wl.heads)
+    b = run_fwd8v(p, q16, k16, codes, vsc, wl.n_tokens, wl.heads)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    c2, s2 = run_prep_v(p, dev["v"])
+    assert torch.equal(c2, codes) and torch.equal(s2, vsc)
+
+
+# ---------------------------------------------------------------------------
+# closed forms at the full 129,410-token size
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def full_shape():
+    wl = W.WORKLOADS[W.HEADLINE]
+    p = problem_for(wl)
+    return wl, p, A.padded_tokens(p)
+
+
+def _e4m3(x):
+    return float(O.e4m3_bits_to_f64(O.e4m3_bits(np.array([x])))[0])
+
+
+def test_fp8v_closed_form_q_zero_v_one(full_shape):
+    wl, p, npad = full_shape
+    n, h = wl.n_tokens, wl.heads
+    qz = torch.zeros((h, npad, 128), dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    k = torch.randn((h, npad, 128), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.ones((n, h, 128), dtype=torch.bfloat16, device="cuda")
+    codes, vsc = run_prep_v(p, v)
+    assert np.all(codes_nhd(codes, n) == 0x7E) and torch.all(vsc == np.float32(1.0) / np.float32(448.0))
+    o = run_fwd8v(p, qz, k, codes, vsc, n, h)
+    # every numerator is 2^0.8, rounded to 1.75; the denominator keeps 2^0.8:
+    # O = 1.75 / 2^0.8 = 1.00511..., whose bf16 rounding is 1 + 2^-7
+    expect = _e4m3(ALPHA) / ALPHA
+    assert abs(expect - 1.0051) < 1e-4
+    assert torch.all(o == 1.0078125), o.float().unique()
+
+
+def test_fp8v_closed_form_q_zero_gives_scaled_mean(full_shape):
+    wl, p, npad = full_shape
+    n, h = wl.n_tokens, wl.heads
+    qz = torch.zeros((h, npad, 128), dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(6)
+    k = torch.randn((h, npad, 128), generator=g, device="cuda").to(torch.bfloat16)
+    mu = torch.rand((1, h, 128), generator=g, device="cuda") * 4 - 2
+    v = (torch.randn((n, h, 128), generator=g, device="cuda") + mu).to(torch.bfloat16)
+    codes, vsc = run_prep_v(p, v)
+    o = run_fwd8v(p, qz, k, codes, vsc, n, h).double().cpu().numpy()
+    vb = W.torch_to_bits(v)
+    f = _e4m3(ALPHA) / ALPHA
+    for hh in (0, h // 2, h - 1):
+        vh = v_hat_of(vb[:, hh, :])
+        expect = f * vh.mean(axis=0)
+        err = np.abs(o[:, hh, :] - expect[None])
+        assert np.all(err <= 2.0 ** -8 * np.abs(expect)[None] + 2e-4 * np.abs(vh).mean(axis=0)[None]), err.max()
+
+
+def test_fp8v_closed_form_last_key_spike(full_shape):
+    wl, p, npad = full_shape
+    n, h = wl.n_tokens, wl.heads
+    # only key N-1 aligns with every query (logit 20, all others 0): its numerator
+    # is 2^0.8 -> 1.75, every other one 2^0.8 e^-20 rounds to 0
+    q = torch.zeros((h, npad, 128), dtype=torch.bfloat16, device="cuda")
+    q[:, :n, 0] = 1.0
+    k = torch.zeros((h, npad, 128), dtype=torch.bfloat16, device="cuda")
+    k[:, n - 1, 0] = 20.0 / SCALE
+    g = torch.Generator(device="cuda").manual_seed(7)
+    v = torch.randn((n, h, 128), generator=g, device="cuda").to(torch.bfloat16)
+    codes, vsc = run_prep_v(p, v)
+    o = run_fwd8v(p, q, k, codes, vsc, n, h).double().cpu().numpy()
+    kf = float(k[0, n - 1, 0].double().item()) * SCALE
+    assert ALPHA * math.exp(-kf) < 2.0 ** -10
+    vb = W.torch_to_bits(v)
+    rows = [0, 1, n // 2, n - 2, n - 1]
+    for hh in (0, h - 1):
+        vlast = v_hat_of(vb[:, hh, :])[n - 1]
+        expect = _e4m3(ALPHA) * vlast / (ALPHA * (1 + (n - 1) * math.exp(-kf)))
+        err = np.abs(o[rows, hh, :] - expect[None])
+        assert np.all(err <= 2.0 ** -8 * np.abs(expect)[None] + 1e-4), err.max()
+
+
+# ---------------------------------------------------------------------------
+# full workloads on sampled rows
+# ---------------------------------------------------------------------------
+
+def _sampled(wl, cfg, int8):
+    from gpu_util import sample_rows
+    inp = W.make_inputs(cfg, wl)
+    N, H = wl.n_tokens, wl.heads
+    print(f"    {wl.name} N={N} H={H} int8={int8}", flush=True)
+    dev = W.device_inputs(inp)
+    p = problem_for(wl, int8=int8)
+    qo, ko, qs, ks = run_prep(p, dev)
+    codes, vsc = run_prep_v(p, dev["v"])
+    o = run_fwd8v(p, qo, ko, codes, vsc, N, H, qs, ks)
+    rows = sample_rows(wl, n_random=64)
+    got_rows = f64(o[torch.from_numpy(rows).cuda()])
+    g, r, b = [], [], []
+    for hh in (0, H - 1):
+        if int8:
+            cq, ck = qo[hh, :N].cpu().numpy(), ko[hh, :N].cpu().numpy()
+            sq, sk = qs[hh].cpu().numpy().astype(np.float64), ks[hh].cpu().numpy().astype(np.float64)
+            s = (O.scores_i32(cq[rows], ck).astype(np.float64) * sq[rows // 64][:, None]
+                 * sk[np.arange(N) // 64][None, :] * SCALE)
+        else:
+            qv, kv = f64(qo[hh, :N]), f64(ko[hh, :N])
+            s = (qv[rows] @ kv.T) * SCALE
+        ref, bound = stage_rows(s, v_hat_of(inp.v[:, hh, :]))
+        g.append(got_rows[:, hh, :])
+        r.append(ref)
+        b.append(bound)
+    check_fp8(np.stack(g), np.stack(r), np.stack(b), what=f"{wl.name} fp8v sampled")
+    assert torch.isfinite(o.float()).all()
+
+
+def test_full_headline_sampled_rows_fp8v():
+    _sampled(W.WORKLOADS[W.HEADLINE], W.HEADLINE, int8=False)
+
+
+def test_full_int8_workload_sampled_rows_fp8v():
+    _sampled(W.WORKLOADS[4], 4, int8=True)

@@ -415,3 +415,101 @@ def test_int8_attention_reduces_to_float_when_lossless():
     got2 = O.attention_i8_rows_head(rows, cq, sq, ck2, sk2, v, 1e-3)
     want2 = O.attention_head(q.astype(np.float64), k2.astype(np.float64), v, 1e-3)
     np.testing.assert_allclose(got2, want2, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# E4M3 encoder / FP8 V quantiser: OCP format values, exhaustive round trip,
+# brute-force nearest value, a library cast, and the format's error bound
+# --------------------------------------------------------------------------
+
+def _e4m3_table():
+    """Every finite E4M3 value with its code, from the bit fields (sign, 4-bit
+    exponent with bias 7, 3-bit mantissa; exponent field 0 is subnormal)."""
+    codes, vals = [], []
+    for b in range(256):
+        e, m = (b >> 3) & 15, b & 7
+        if e == 15 and m == 7:
+            continue                                    # NaN
+        mag = m / 8.0 * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        codes.append(b)
+        vals.append(-mag if b & 0x80 else mag)
+    return np.array(codes, dtype=np.uint8), np.array(vals)
+
+
+def test_e4m3_format_values():
+    cases = [(448.0, 0x7E), (-448.0, 0xFE), (1.0, 0x38), (2.0 ** -6, 0x08), (2.0 ** -9, 0x01),
+             (7 * 2.0 ** -9, 0x07), (0.0, 0x00), (-0.0, 0x80), (240.0, 0x77), (1.75, 0x3E), (0.5, 0x30)]
+    xs = np.array([c[0] for c in cases])
+    got = O.e4m3_bits(xs)
+    assert [int(g) for g in got] == [c[1] for c in cases]
+    dec = O.e4m3_bits_to_f64(np.array([c[1] for c in cases], dtype=np.uint8))
+    assert np.array_equal(dec, xs) and np.array_equal(np.signbit(dec), np.signbit(xs))
+    with pytest.raises(ValueError):
+        O.e4m3_bits(np.array([449.0]))
+    with pytest.raises(ValueError):
+        O.e4m3_bits_to_f64(np.array([0x7F], dtype=np.uint8))
+
+
+def test_e4m3_exhaustive_round_trip_and_sign_symmetry():
+    codes, vals = _e4m3_table()
+    assert len(codes) == 254
+    assert np.array_equal(O.e4m3_bits_to_f64(codes), vals)
+    assert np.array_equal(O.e4m3_bits(vals), codes)
+    x = np.random.default_rng(40).uniform(0, 448, 20000)
+    assert np.array_equal(O.e4m3_bits(-x), O.e4m3_bits(x) | 0x80)
+
+
+def test_e4m3_ties_go_to_even_mantissa():
+    # midpoints between neighbours: the one with an even mantissa field wins
+    pairs = [(1.0625, 0x38), (1.1875, 0x3A), (1.5 * 2.0 ** -9, 0x02), (0.5 * 2.0 ** -9, 0x00),
+             (7.5 * 2.0 ** -9, 0x08), (432.0, 0x7E), (2.0 ** -6 * (1 + 1 / 16), 0x08)]
+    for x, code in pairs:
+        assert int(O.e4m3_bits(np.array([x]))[0]) == code, x
+    # 0.484375 lies between 0.46875 (0x2F, mantissa 7) and 0.5 (0x30): ties to 0.5
+    assert int(O.e4m3_bits(np.array([0.484375]))[0]) == 0x30
+
+
+def test_e4m3_brute_force_nearest_value():
+    """Nearest finite value by exhaustive search; exact ties broken to the even code."""
+    codes, vals = _e4m3_table()
+    rng = np.random.default_rng(41)
+    x = np.concatenate([rng.uniform(-448, 448, 3000), rng.uniform(-0.05, 0.05, 3000),
+                        np.ldexp(rng.uniform(-1, 1, 2000), rng.integers(-12, 9, 2000))]).astype(np.float32)
+    got = O.e4m3_bits(x.astype(np.float64))
+    for xi, g in zip(x.astype(np.float64), got):
+        d = np.abs(vals - xi)
+        best = np.nonzero(d == d.min())[0]
+        cand = [c for c in codes[best] if (c & 0x80) == (0x80 if np.signbit(xi) else 0) or xi == 0] or list(codes[best])
+        if len(cand) > 1:
+            cand = [c for c in cand if (c & 1) == 0]
+        assert int(g) in [int(c) for c in cand], (xi, g, cand)
+
+
+def test_e4m3_matches_torch_float8_cast():
+    rng = np.random.default_rng(42)
+    x = np.concatenate([rng.uniform(-448, 448, 200000), rng.uniform(-2.0 ** -5, 2.0 ** -5, 100000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_bits(x.astype(np.float64)), ref)
+
+
+def test_quantize_v_fp8_hand_cases_and_bound():
+    v = np.zeros((5, 4), dtype=np.float32)
+    v[:, 0] = [1.0, -2.0, 0.5, 0.0, 0.25]          # absmax 2 -> scale 2/448, 1.0 -> 224
+    v[:, 1] = [0.0] * 5                            # zero channel: scale 0, codes 0
+    v[:, 2] = [-3.0, 1.0, 3.0, 0.0, 0.0]
+    v[:, 3] = [1e-3, 0, 0, 0, 0]
+    codes, scales = O.quantize_v_fp8(v)
+    assert scales[0] == np.float32(2.0) / np.float32(448.0)
+    assert scales[1] == 0 and np.all(codes[:, 1] == 0)
+    assert int(codes[1, 0]) == 0xFE and int(codes[2, 2]) == 0x7E and int(codes[0, 2]) == 0xFE
+    assert int(codes[0, 0]) == 0x76                 # 224 = 1.75 * 2^7: exponent field 14, mantissa 6
+    assert int(codes[0, 3]) == 0x7E                 # a lone value is its channel's absmax
+    # the format's bound: relative 2^-4 for normal codes, absolute 2^-10 * scale below
+    rng = np.random.default_rng(43)
+    x = (rng.standard_normal((3000, 128)) * rng.uniform(0.01, 50, size=(1, 128))).astype(np.float32)
+    c, s = O.quantize_v_fp8(x)
+    deq = O.dequantize_v_fp8(c, s)
+    err = np.abs(deq - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, s[None, :].astype(np.float64) * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    assert np.all(np.max(np.abs(deq), axis=0) == 448.0 * s.astype(np.float64))
