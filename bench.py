@@ -6,11 +6,14 @@ h3attn_forward (non-causal attention over the whole packed sequence) on one
 batch of seeded synthetic inputs already resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+                    [--qk bf16|int8] [--pv bf16|fp8] [--headline-only]
 
 Prints one JSON line.  ``value`` is attention TFLOP/s (4 N^2 d H per step)
 over the whole step; ``roofline`` rates the forward kernel alone against the
-bf16 matrix-core peak; ``cpu_baseline`` times the CPU oracle on a bounded
-sample of the same workload.
+matrix-core peak of its operand types (bf16 by default; with --qk int8 or
+--pv fp8 the harmonic mean of the two halves' rates); ``per_config`` times the
+other workloads, head shards and FP8 P V variants; ``cpu_baseline`` times the
+CPU oracle on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -24,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
 PEAK_INT8_TOPS = 5033.2
+PEAK_FP8_TFLOPS = 5033.2      # dense E4M3 matrix-core rate
 PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per h3attn_forward launch on the 1344x768/124-frame bf16 workload,
@@ -35,9 +39,9 @@ PEAK_HBM_GBS = 8000.0
 # csrc/forward.hip no longer hashes to `source_sha256`, traffic is null.
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
-    "source_sha256": "d01289f46279ed5a25c86cf2f2375b543a0271fe544e0a6a7ed7fdf34ded0a5c",
-    "fetch_kib": 13337121.4, "fetch_scale": 2.0,
-    "write_kib": 828294.5, "write_scale": 1.0,
+    "source_sha256": "e1827f2981649a473976c158f59adafff2573b965dc1232d47df6b60bbabb3f6",
+    "fetch_kib": 13340384.9, "fetch_scale": 2.0,
+    "write_kib": 818340.8, "write_scale": 1.0,
 }
 
 
@@ -69,6 +73,10 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=6)
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the per-configuration sweep (other workloads, head shards, block-24 shape)")
+    ap.add_argument("--qk", choices=("bf16", "int8"), default=None,
+                    help="Q/K format of the timed step (default: the workload's own)")
+    ap.add_argument("--pv", choices=("bf16", "fp8"), default="bf16",
+                    help="P V product: bf16, or E4M3 V (staged each step) on the FP8 matrix cores")
     ap.add_argument("--copy-probe", type=int, default=None, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration) and exit")
     return ap.parse_args()
@@ -125,8 +133,20 @@ def cpu_baseline(wl, cfg, inp, rows_n, heads_n):
                       f"prep of every key included), fp64 numpy, {dt:.1f} s"}
 
 
-def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=None):
-    """HIP-event times (ms) of prep and forward over `steps` calls after `warmup`."""
+def mixed_peak(int8, fp8v):
+    """Matrix-core peak of a step whose Q K^T half runs at the Q/K rate and whose
+    P V half runs at the P V rate (equal FLOP counts): their harmonic mean."""
+    qk = PEAK_INT8_TOPS if int8 else PEAK_BF16_TFLOPS
+    pv = PEAK_FP8_TFLOPS if fp8v else PEAK_BF16_TFLOPS
+    return 2.0 / (1.0 / qk + 1.0 / pv)
+
+
+def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=None, vfp8=None):
+    """HIP-event times (ms) of prep and forward over `steps` calls after `warmup`.
+
+    With ``vfp8 = (codes, scales)`` each step also stages V as E4M3 (timed on
+    its own) and runs the FP8 P V forward; the third list holds those times.
+    """
     import torch
     q, k, v = dev["q"], dev["k"], dev["v"]
     if heads is not None:                     # one GPU's share of the heads: strided views
@@ -134,52 +154,78 @@ def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=No
     ev = lambda: torch.cuda.Event(enable_timing=True)
     out = []
     for i in range(warmup + steps):
-        e0, e1, e2 = ev(), ev(), ev()
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record()
         A.prep(p, q, k, dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
         e1.record()
-        A.forward(p, q_out, k_out, v, o, scale, qs, ks)
+        if vfp8 is not None:
+            A.prep_v_fp8(p, v, vfp8[0], vfp8[1])
         e2.record()
+        if vfp8 is None:
+            A.forward(p, q_out, k_out, v, o, scale, qs, ks)
+        else:
+            A.forward_fp8v(p, q_out, k_out, vfp8[0], vfp8[1], o, scale, qs, ks)
+        e3.record()
         if i >= warmup:
-            out.append((e0, e1, e2))
+            out.append((e0, e1, e2, e3))
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b, _ in out], [b.elapsed_time(c) for _, b, c in out]
+    return ([a.elapsed_time(b) for a, b, _, _ in out], [c.elapsed_time(d) for _, _, c, d in out],
+            [b.elapsed_time(c) for _, b, c, _ in out])
 
 
 def sweep(A, W, headline_dev, steps=3, warmup=1):
     """Forward throughput of every other workload: the remaining configurations,
-    the headline's per-GPU head shards and the pages' block-24 shape."""
+    the headline's per-GPU head shards, the pages' block-24 shape, and the FP8
+    P V variants (V staged as E4M3) on the headline, the 243-frame int8
+    workload and the block-24 shape."""
     import statistics
     import torch
     scale = 1.0 / math.sqrt(128.0)
     rows = []
-    jobs = [(i, W.WORKLOADS[i], None) for i in range(len(W.WORKLOADS)) if i != W.HEADLINE]
-    jobs += [(W.HEADLINE, w, w.heads) for w in W.SHARDS]
-    jobs += [(100, W.BLOCK24, None)]
-    for cfg, wl, shard_heads in jobs:
-        print(f"[bench] sweep {wl.name}: N={wl.n_tokens} H={wl.heads}", file=sys.stderr, flush=True)
-        if shard_heads is None:
-            dev = W.device_inputs(W.make_inputs(cfg, wl, threads=16))
-        else:
+    # (seed, workload, head share of the headline tensors, Q/K int8, FP8 P V)
+    hl = W.WORKLOADS[W.HEADLINE]
+    jobs = [(i, W.WORKLOADS[i], None, W.WORKLOADS[i].qk_int8, False)
+            for i in range(len(W.WORKLOADS)) if i != W.HEADLINE]
+    jobs += [(4, W.WORKLOADS[4], None, True, True)]
+    jobs += [(W.HEADLINE, w, w.heads, False, False) for w in W.SHARDS]
+    jobs += [(W.HEADLINE, hl, hl.heads, False, True), (W.HEADLINE, hl, hl.heads, True, True)]
+    jobs += [(100, W.BLOCK24, None, False, False), (100, W.BLOCK24, None, True, True)]
+    cache = {}
+    for cfg, wl, shard_heads, int8, fp8v in jobs:
+        print(f"[bench] sweep {wl.name}: N={wl.n_tokens} H={wl.heads} qk={'int8' if int8 else 'bf16'} "
+              f"pv={'fp8' if fp8v else 'bf16'}", file=sys.stderr, flush=True)
+        if shard_heads is not None:
             dev = headline_dev
-        fmt = A.QK_I8_BLK64 if wl.qk_int8 else A.QK_BF16
+        else:
+            if cfg not in cache:
+                cache.clear()
+                torch.cuda.empty_cache()
+                cache[cfg] = W.device_inputs(W.make_inputs(cfg, wl, threads=16))
+            dev = cache[cfg]
+        fmt = A.QK_I8_BLK64 if int8 else A.QK_BF16
         p = A.problem(wl.n_tokens, wl.heads, fmt)
         q_out, k_out, qs, ks = A.alloc_prepped(p)
+        vfp8 = A.alloc_v_fp8(p) if fp8v else None
         o = torch.empty((wl.n_tokens, wl.heads, 128), dtype=torch.bfloat16, device="cuda")
-        prep_ms, fwd_ms = time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, shard_heads)
+        prep_ms, fwd_ms, prepv_ms = time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup,
+                                              shard_heads, vfp8)
         med = statistics.median(fwd_ms)
         tf = wl.flops / (med * 1e-3) / 1e12
         row = {"workload": wl.name, "n_tokens": wl.n_tokens, "heads": wl.heads,
-               "qk": "int8" if wl.qk_int8 else "bf16", "steps": steps,
+               "qk": "int8" if int8 else "bf16", "pv": "fp8" if fp8v else "bf16", "steps": steps,
                "forward_ms": {"median": round(med, 4), "min": round(min(fwd_ms), 4), "max": round(max(fwd_ms), 4)},
                "prep_ms": round(statistics.median(prep_ms), 4),
                "forward_tflops": round(tf, 2), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
-        if wl.qk_int8:
-            # half the work (Q K^T) at the int8 rate, half (P V) at the bf16 rate
-            ideal_ms = (wl.flops / 2 / (PEAK_INT8_TOPS * 1e12) + wl.flops / 2 / (PEAK_BF16_TFLOPS * 1e12)) * 1e3
+        if fp8v:
+            row["prep_v_ms"] = round(statistics.median(prepv_ms), 4)
+        if int8 or fp8v:
+            # half the work (Q K^T) at the Q/K rate, half (P V) at the P V rate
+            qk_peak = PEAK_INT8_TOPS if int8 else PEAK_BF16_TFLOPS
+            pv_peak = PEAK_FP8_TFLOPS if fp8v else PEAK_BF16_TFLOPS
+            ideal_ms = (wl.flops / 2 / (qk_peak * 1e12) + wl.flops / 2 / (pv_peak * 1e12)) * 1e3
             row["pct_mixed_peak"] = round(100 * ideal_ms / med, 2)
         rows.append(row)
-        del dev, q_out, k_out, qs, ks, o
+        del q_out, k_out, qs, ks, o, vfp8
         torch.cuda.empty_cache()
     return rows
 
@@ -202,12 +248,15 @@ def main():
 
     cfg = W.HEADLINE if args.config is None else args.config
     wl = W.WORKLOADS[cfg]
+    int8 = wl.qk_int8 if args.qk is None else args.qk == "int8"
+    fp8v = args.pv == "fp8"
     print(f"[bench] generating {wl.name}: N={wl.n_tokens} H={wl.heads}", file=sys.stderr, flush=True)
     inp = W.make_inputs(cfg, threads=16)
     dev = W.device_inputs(inp)
-    fmt = A.QK_I8_BLK64 if wl.qk_int8 else A.QK_BF16
+    fmt = A.QK_I8_BLK64 if int8 else A.QK_BF16
     p = A.problem(wl.n_tokens, wl.heads, fmt)
     q_out, k_out, qs, ks = A.alloc_prepped(p)
+    v_codes, v_scales = A.alloc_v_fp8(p) if fp8v else (None, None)
     o = torch.empty_like(dev["v"])
     scale = 1.0 / math.sqrt(128.0)
 
@@ -218,9 +267,14 @@ def main():
             e0, e1, e2 = ev(), ev(), ev()
             e0.record()
         A.prep(p, dev["q"], dev["k"], dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
+        if fp8v:
+            A.prep_v_fp8(p, dev["v"], v_codes, v_scales)
         if timed is not None:
             e1.record()
-        A.forward(p, q_out, k_out, dev["v"], o, scale, qs, ks)
+        if fp8v:
+            A.forward_fp8v(p, q_out, k_out, v_codes, v_scales, o, scale, qs, ks)
+        else:
+            A.forward(p, q_out, k_out, dev["v"], o, scale, qs, ks)
         if timed is not None:
             e2.record()
             timed.append((e0, e1, e2))
@@ -248,11 +302,14 @@ def main():
     flops = wl.flops
     value = flops / (ms_step * 1e-3) / 1e12
     fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
-    peak = PEAK_INT8_TOPS if wl.qk_int8 else PEAK_BF16_TFLOPS
-    # prep: algorithmic bytes = read Q and K (bf16), write Q' and K' (+ scales in int8)
+    peak = mixed_peak(int8, fp8v)
+    # prep: algorithmic bytes = read Q and K (bf16), write Q' and K' (+ scales in int8);
+    # with FP8 P V also read V and write its codes and channel scales
     n, h = wl.n_tokens, wl.heads
-    prep_bytes = 2 * n * h * 128 * 2 + 2 * n * h * 128 * (1 if wl.qk_int8 else 2) + \
-        (2 * h * ((n + 63) // 64) * 4 if wl.qk_int8 else 0)
+    prep_bytes = 2 * n * h * 128 * 2 + 2 * n * h * 128 * (1 if int8 else 2) + \
+        (2 * h * ((n + 63) // 64) * 4 if int8 else 0) + \
+        (n * h * 128 * 3 + h * 128 * 4 if fp8v else 0)
+    dtype = "bf16" if not (int8 or fp8v) else f"{'int8' if int8 else 'bf16'}-qk/{'fp8' if fp8v else 'bf16'}-pv"
 
     res = {
         "metric": "attention TFLOP/s and % bf16 MFMA peak at 129k packed tokens, 24 heads, d=128",
@@ -265,7 +322,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8-qk/bf16-pv" if wl.qk_int8 else "bf16",
+        "dtype": dtype,
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V, gamma ~ N(1,0.1))",
         "config": {"workload": wl.name, "n_tokens": n, "heads": h, "head_dim": 128, "batch": 1,
                    "video_grid": list(wl.grid), "audio_tokens": wl.audio, "text_tokens": wl.text,
@@ -275,14 +332,14 @@ def main():
                     "prep_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "mfma", "kernel": "h3attn_forward", "achieved": round(fwd_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(fwd_tflops / peak, 4),
-                     "traffic": forward_traffic(wl.name),
+                     "traffic": forward_traffic(wl.name) if not (int8 or fp8v) else None,
                      "algorithmic_bytes": 4 * n * h * 128 * 2},
     }
     fwd_all = [b.elapsed_time(c) for _, b, c in timed]
     res["kernels"]["forward_ms_min"] = round(min(fwd_all), 4)
     res["kernels"]["forward_ms_max"] = round(max(fwd_all), 4)
     res["kernels"]["forward_ms_median"] = round(sorted(fwd_all)[len(fwd_all) // 2], 4)
-    if not args.headline_only and args.config is None:
+    if not args.headline_only and args.config is None and not (int8 or fp8v):
         res["per_config"] = sweep(A, W, dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
