@@ -322,6 +322,12 @@ fwd8_kernel(FwdParams P) {
     float qscale = 1.f;
     if constexpr (kInt8) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
     const float* kscale = kInt8 ? P.ks + (int64_t)head * P.nblk : nullptr;
+    // All loads above complete here, and the compiler knows it.  Otherwise its
+    // wait-count bookkeeping carries the Q' loads into the tile loop as possibly
+    // outstanding and waits for them with vmcnt(7..0) between the Q K^T
+    // products of every tile; vmcnt also counts the buffer -> LDS copies (asm,
+    // invisible to it), so vmcnt(0) would wait for the tile fetched three ahead.
+    __builtin_amdgcn_s_waitcnt(0);
 
     f32x16 O[4];
 #pragma unroll
