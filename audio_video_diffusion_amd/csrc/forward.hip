@@ -24,9 +24,10 @@
 //                                        (int8: v_mfma_i32_32x32x32_i8)
 //     O^T (d x queries)   += V^T P^T     with v_mfma_f32_32x32x16_bf16
 //   The row max and row sum of a query are in-lane reductions plus one
-//   exchange between lane l and l^32, and the rescale of O touches only the
-//   lane's own accumulators.  V^T operands are read from the row-major V
-//   tile with ds_read_b64_tr_b16, which transposes as it reads;
+//   exchange between lane l and l^32 (v_permlane32_swap), and the rescale of
+//   O touches only the lane's own accumulators.  V^T operands are read from
+//   the row-major V tile with ds_read_b64_tr_b16, which transposes as it
+//   reads;
 // * K' rows are placed in LDS so that the 32x32 accumulator layout of S^T
 //   (lane half h holds rows 8i+4h+j) directly yields, per lane, 8 consecutive
 //   keys for each 16-key step of the P V product: P needs no lane movement;
@@ -199,6 +200,18 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
     }
 }
 
+// max / sum of x over lanes l and l ^ 32, in every lane: v_permlane32_swap
+// exchanges the two lane halves on the VALU (no LDS round trip, which would
+// queue behind the tile's operand reads)
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most kOutstanding of this wave's DMA instructions are still in
 // flight (vmcnt retires in issue order): with the two newest fetches allowed
@@ -321,7 +334,11 @@ fwd8_kernel(FwdParams P) {
         q[t] = __builtin_bit_cast(QOp, ld16(qhead + (int64_t)(q0 + n32) * D::kRowB + 32 * t + 16 * hh));
     float qscale = 1.f;
     if constexpr (kInt8) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
-    const float* kscale = kInt8 ? P.ks + (int64_t)head * P.nblk : nullptr;
+    // K block scales through the constant address space: one scalar load per
+    // tile, counted by lgkmcnt.  A vector load would be waited for with
+    // vmcnt(0), which also drains the buffer -> LDS prefetch.
+    typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+    const const_f32_ptr kscale = kInt8 ? (const_f32_ptr)(P.ks + (int64_t)head * P.nblk) : nullptr;
     // All loads above complete here, and the compiler knows it.  Otherwise its
     // wait-count bookkeeping carries the Q' loads into the tile loop as possibly
     // outstanding and waits for them with vmcnt(7..0) between the Q K^T
@@ -339,6 +356,7 @@ fwd8_kernel(FwdParams P) {
     const bool ragged = (n % kBN) != 0;
 
     const D dmo(wave, lane, P.v_st, last * kBN, n);
+    float ks_cur = kInt8 ? kscale[0] : 1.f;
     auto fetch = [&](int t) {
         const int kt = min(t, last);
         const u32x4 kr = raw_rsrc(khead + (int64_t)kt * kKTileB);
@@ -407,7 +425,11 @@ fwd8_kernel(FwdParams P) {
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]), "+v"(S[1]));
         }
         // base-2 logit scale of this tile (int8: times the two block scales)
-        const float coef = kInt8 ? P.c * qscale * kscale[j] : P.c;
+        float coef = P.c;
+        if constexpr (kInt8) {
+            coef = P.c * qscale * ks_cur;
+            ks_cur = kscale[min(j + 1, last)];     // the next tile's scale, loaded a tile early
+        }
         if (masked) {
             // keys >= N: the most negative finite score for the max, probability 0 below
 #pragma unroll
@@ -421,7 +443,7 @@ fwd8_kernel(FwdParams P) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kb][e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * coef;
+        mx = max_halves(mx) * coef;
         if (__any(mx > m + kRescaleLog2)) {
             const float mm = fmaxf(m, mx);
             const float alpha = __builtin_amdgcn_exp2f(m - mm);
@@ -530,7 +552,7 @@ fwd8_kernel(FwdParams P) {
     // >= N are switched off: this empty statement consumes O before it.
     asm volatile("" ::"a"(O[0]), "a"(O[1]), "a"(O[2]), "a"(O[3]));
 
-    const float lt = l + __shfl_xor(l, 32);
+    const float lt = sum_halves(l);
     const float inv = 1.0f / lt;
     const int qrow = q0 + n32;
     if (qrow < n) {
