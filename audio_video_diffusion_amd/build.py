@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libh3attn.so")
-SOURCES = ("api.hip", "prep.hip", "prep_v.hip", "forward.hip")
+SOURCES = ("api.hip", "prep.hip", "prep_v.hip", "forward.hip", "calib.hip")
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code.  No fast-math: the

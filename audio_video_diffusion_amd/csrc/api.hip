@@ -268,6 +268,15 @@ int h3attn_prep_v_fp8(const h3attn_problem* p, const void* v, int64_t v_stride_t
     return H3ATTN_OK;
 }
 
+int h3attn_calibrate_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* stream) {
+    if (!out) return H3ATTN_E_NULL;
+    if (!aligned(out, 4)) return H3ATTN_E_ALIGN;
+    if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20)) return H3ATTN_E_SHAPE;
+    if (h3::launch_mfma_calib(out, blocks, iters, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return H3ATTN_E_HIP;
+    return H3ATTN_OK;
+}
+
 int h3attn_debug_scores_i32(const h3attn_problem* p, const void* q_codes, const void* k_codes,
                             int32_t head, int32_t row0, int32_t nrows, int32_t col0, int32_t ncols,
                             int32_t* out, void* stream) {

@@ -52,5 +52,6 @@ hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream);
 hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t stream);
 hipError_t launch_prep_v(const PrepVParams& P, hipStream_t stream);
 hipError_t launch_scores_i8(const ScoreParams& P, hipStream_t stream);
+hipError_t launch_mfma_calib(float* out, int blocks, int iters, hipStream_t stream);
 
 }  // namespace h3

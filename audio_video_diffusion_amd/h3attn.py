@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG, "libh3attn.so")
 
 QK_BF16 = 0
 QK_I8_BLK64 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_UNSUPPORTED", -4: "E_ALIGN",
           -5: "E_ALIAS", -6: "E_HIP"}
@@ -90,6 +90,7 @@ def _load():
         "h3attn_prep_v_fp8": (ctypes.c_int, [pp, vp, i64, i64, vp, vp, vp]),
         "h3attn_forward_fp8v": (ctypes.c_int, [pp, vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, vp]),
         "h3attn_debug_scores_i32": (ctypes.c_int, [pp, vp, vp, i32, i32, i32, i32, i32, vp, vp]),
+        "h3attn_calibrate_mfma_bf16": (ctypes.c_int, [i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -220,3 +221,13 @@ def debug_scores_i32(p: Problem, q_codes, k_codes, head: int, row0: int, nrows: 
                                       nrows, col0, ncols, _ptr(out), _stream(stream))
     if rc:
         raise H3AttnError(rc, "h3attn_debug_scores_i32")
+
+
+def calibrate_mfma_bf16(blocks: int, iters: int, out, stream=None):
+    """``h3attn_calibrate_mfma_bf16`` into ``out`` (fp32, >= blocks * 512 elements); returns its FLOP count."""
+    if out.numel() < blocks * 512:
+        raise ValueError("out holds fewer than blocks * 512 floats")
+    rc = _lib.h3attn_calibrate_mfma_bf16(blocks, iters, _ptr(out), _stream(stream))
+    if rc:
+        raise H3AttnError(rc, "h3attn_calibrate_mfma_bf16")
+    return blocks * 8 * iters * 16 * 32768.0

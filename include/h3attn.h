@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 2
+#define H3ATTN_ABI_VERSION 3
 
 typedef enum {
     H3ATTN_OK = 0,
@@ -242,6 +242,18 @@ int h3attn_debug_scores_i32(const h3attn_problem* p,
 
 /* Static description of a status code (never NULL). */
 const char* h3attn_status_string(int status);
+
+/*
+ * h3attn_calibrate_mfma_bf16 - measurement aid, not part of the attention
+ * path: `blocks` work-groups of 512 threads (two waves per SIMD, as the
+ * forward) each run `iters` x 16 bf16 32x32x16 matrix-core products per wave
+ * on register operands, i.e. blocks * 8 * iters * 16 * 32768 FLOP, so that a
+ * caller timing it on `stream` gets the sustained bf16 MFMA rate of this GPU
+ * under its power and clock limits.
+ * out: device, fp32 [blocks * 512], 4-byte aligned (written with the sums).
+ * Errors: E_NULL, E_ALIGN; E_SHAPE unless 1 <= blocks, iters <= 2^20; E_HIP.
+ */
+int h3attn_calibrate_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* stream);
 
 /* H3ATTN_ABI_VERSION of the built library. */
 int h3attn_abi_version(void);

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 2
+    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 3
     for s in (0, -1, -2, -3, -4, -5, -6, 7):
         assert A.lib.h3attn_status_string(s)
 
@@ -179,6 +179,15 @@ def test_forward_fp8v_checks():
     assert fwd8v(p, o=J - 64) == -5                            # output over the V scales
     p8 = A.problem(1000, 3, A.QK_I8_BLK64)
     assert fwd8v(p8) == -1
+
+
+def test_calibration_checks():
+    call = A.lib.h3attn_calibrate_mfma_bf16
+    assert call(8, 10, None, None) == -1
+    assert call(8, 10, K + 2, None) == -4
+    assert call(0, 10, K, None) == -2
+    assert call(8, 0, K, None) == -2
+    assert call((1 << 20) + 1, 10, K, None) == -2
 
 
 def test_debug_scores_checks():
