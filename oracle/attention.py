@@ -25,6 +25,11 @@ pages "H3 Runtime Current State" and "H3 Blackwell Runtime Plan"):
    Kernels: V scale/FP8 quantization; the V-preparation study emits E4M3 V plus
    FP32 per-channel scales).  The GPU also rounds P to E4M3 inside its P V
    product; the oracle keeps P exact, as it keeps P exact against bf16.
+6. Optional K smoothing before the int8 K quantisation: subtract the per-head,
+   per-channel mean of K' over all tokens (the K-mean step of the same path:
+   "H3 Runtime Current State", Owned Performance Kernels, K mean).  Every
+   score of a query row moves by the same q . mean, so the softmax, and the
+   exact attention, do not change; only the quantisation error does.
 
 All floating point is fp64 except where the method fixes fp32 (the int8
 quantiser, whose rounding decisions must match bit for bit).
@@ -40,6 +45,11 @@ the design notes of the repository):
 * Int8: round-half-even, symmetric +-127, blocks of 64 tokens from token 0
   with a partial last block, scale = fl32(absmax/127), codes =
   rint(fl32(x * fl32(127/absmax))), an all-zero block has scale 0 and codes 0.
+* K smoothing: the mean is taken of the bf16-rounded prepped K' (the int8
+  quantiser's input), in float32 and in a fixed order: a sequential sum over
+  each 64-token block in token order, a sequential sum of the block sums in
+  block order, then one IEEE division by N.  The quantiser then sees
+  fl32(k - mean) in place of k.
 * FP8 V: per head and channel over all N tokens, scale = fl32(absmax/448),
   value = clamp(fl32(v * fl32(448/absmax)), -448, 448), rounded to the nearest
   E4M3 value (ties to even mantissa, subnormals kept); an all-zero channel has
@@ -55,6 +65,7 @@ __all__ = [
     "softmax_rows", "attention", "attention_head", "attention_rows_head",
     "quantize_i8", "scores_i32", "attention_i8_rows_head",
     "e4m3_bits", "e4m3_bits_to_f64", "quantize_v_fp8", "dequantize_v_fp8",
+    "k_mean_blocked", "smooth_k",
 ]
 
 
@@ -353,3 +364,34 @@ def quantize_v_fp8(v: np.ndarray):
 def dequantize_v_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """The V the FP8 P V product multiplies: code value times channel scale (float64)."""
     return e4m3_bits_to_f64(codes) * scales.astype(np.float64)[None, :]
+
+
+# ----------------------------------------------------------------------------
+# K smoothing (softmax-invariant mean subtraction before the int8 K quantiser)
+# ----------------------------------------------------------------------------
+
+def k_mean_blocked(k: np.ndarray, block: int = QUANT_BLOCK) -> np.ndarray:
+    """Per-channel mean of one head's K' (float32 [N, d], bf16-valued), float32.
+
+    Fixed order, one float32 rounding per addition: each block of ``block``
+    tokens is summed sequentially in token order (numpy's cumsum is a plain
+    running sum), the block sums are summed sequentially in block order, and
+    the total is divided by N (IEEE float32 division).
+    """
+    k = np.asarray(k)
+    if k.dtype != np.float32:
+        raise TypeError("k_mean_blocked expects float32 input")
+    n, d = k.shape
+    if n == 0:
+        raise ValueError("no tokens")
+    sums = [np.cumsum(k[b:b + block], axis=0, dtype=np.float32)[-1] for b in range(0, n, block)]
+    total = np.cumsum(np.stack(sums), axis=0, dtype=np.float32)[-1]
+    return (total / np.float32(n)).astype(np.float32)
+
+
+def smooth_k(k: np.ndarray, block: int = QUANT_BLOCK):
+    """(mean, k - mean) of one head's K' in float32: the int8 quantiser's input
+    after K smoothing (each difference rounded once to float32)."""
+    mu = k_mean_blocked(k, block)
+    return mu, (np.asarray(k, dtype=np.float32) - mu[None, :]).astype(np.float32)
+

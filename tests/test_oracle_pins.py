@@ -513,3 +513,66 @@ def test_quantize_v_fp8_hand_cases_and_bound():
     bound = np.maximum(np.abs(x) * 2.0 ** -4, s[None, :].astype(np.float64) * 2.0 ** -10) * (1 + 1e-6)
     assert np.all(err <= bound)
     assert np.all(np.max(np.abs(deq), axis=0) == 448.0 * s.astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# K smoothing: the fixed-order mean, a scalar route, exactness bound,
+# softmax invariance, and its effect on the int8 quantisation error
+# --------------------------------------------------------------------------
+
+def _mean_scalar(col, block=64):
+    """Per-channel mean with numpy float32 scalars, one addition at a time."""
+    blocks = []
+    for b in range(0, len(col), block):
+        s = np.float32(0.0)
+        for v in col[b:b + block]:
+            s = np.float32(s + np.float32(v))
+        blocks.append(s)
+    t = np.float32(0.0)
+    for s in blocks:
+        t = np.float32(t + s)
+    return np.float32(t / np.float32(len(col)))
+
+
+def test_k_mean_blocked_matches_scalar_route_and_bound():
+    rng = np.random.default_rng(50)
+    for n in (1, 63, 64, 65, 200):
+        x = O.bf16_bits_to_f64(O.f32_to_bf16_bits(
+            (rng.standard_normal((n, 6)) * 3 + rng.uniform(-5, 5, 6)).astype(np.float32))).astype(np.float32)
+        mu = O.k_mean_blocked(x)
+        for c in range(6):
+            assert mu[c] == _mean_scalar(x[:, c]), (n, c)
+        exact = x.astype(np.float64).mean(axis=0)
+        # a running float32 sum of m terms is within m * 2^-24 * sum|x| of the exact sum
+        bound = (n + 1) * 2.0 ** -24 * np.abs(x.astype(np.float64)).sum(axis=0) / n + 2.0 ** -24 * np.abs(exact)
+        assert np.all(np.abs(mu - exact) <= bound)
+    mu, xs = O.smooth_k(np.array([[1.0, -2.0], [3.0, 4.0]], dtype=np.float32))
+    assert list(mu) == [2.0, 1.0] and xs.tolist() == [[-1.0, -3.0], [1.0, 3.0]]
+
+
+def test_k_smoothing_is_softmax_invariant():
+    rng = np.random.default_rng(51)
+    n, d = 300, 128
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    k += rng.uniform(-3, 3, d)[None, :]
+    mu = k.mean(axis=0)
+    a = O.attention_head(q, k, v, 0.09)
+    b = O.attention_head(q, k - mu[None, :], v, 0.09)
+    np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13)
+
+
+def test_k_smoothing_lowers_int8_error_on_biased_keys():
+    # a channel-wise offset much larger than the spread: without smoothing the
+    # block absmax is dominated by it; after subtracting the mean the codes
+    # resolve the spread, and the int32 scores (offset by a row constant) stay exact
+    rng = np.random.default_rng(52)
+    n, d = 256, 128
+    k = (rng.standard_normal((n, d)) * 0.3 + rng.uniform(2, 6, d)[None, :]).astype(np.float32)
+    k = O.bf16_bits_to_f64(O.f32_to_bf16_bits(k)).astype(np.float32)
+    c0, s0 = O.quantize_i8(k)
+    mu, ks = O.smooth_k(k)
+    c1, s1 = O.quantize_i8(ks)
+    blk = np.arange(n) // 64
+    e0 = np.abs(c0 * s0[blk][:, None].astype(np.float64) - k)
+    e1 = np.abs(c1 * s1[blk][:, None].astype(np.float64) + mu[None, :].astype(np.float64) - k)
+    assert e1.mean() < 0.2 * e0.mean()
