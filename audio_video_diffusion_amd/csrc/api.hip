@@ -110,16 +110,24 @@ size_t h3attn_v_scales_bytes(const h3attn_problem* p) {
     return (size_t)p->n_heads * 128 * sizeof(float);
 }
 
-int h3attn_prep(const h3attn_problem* p,
+}  // extern "C"
+
+namespace {
+
+// Shared by h3attn_prep and h3attn_prep_ksmooth (int8 with K smoothing).
+int prep_common(const h3attn_problem* p,
                 const void* q, int64_t q_stride_tok, int64_t q_stride_head,
                 const void* k, int64_t k_stride_tok, int64_t k_stride_head,
                 const void* gamma_q, const void* gamma_k, int64_t gamma_head_stride,
                 const int32_t* pos_thw,
                 void* q_out, void* k_out, float* q_scales, float* k_scales,
-                void* stream) {
+                float* k_mean, bool smooth, void* stream) {
     int rc = check_problem(p);
     if (rc) return rc;
     const bool i8 = p->qk_format == H3ATTN_QK_I8_BLK64;
+    if (smooth && !i8) return H3ATTN_E_UNSUPPORTED;
+    if (smooth && !k_mean) return H3ATTN_E_NULL;
+    if (smooth && !aligned(k_mean, 4)) return H3ATTN_E_ALIGN;
     if ((rc = check_in_view(q, q_stride_tok, q_stride_head))) return rc;
     if ((rc = check_in_view(k, k_stride_tok, k_stride_head))) return rc;
     if ((rc = check_in_view(gamma_q, 0, gamma_head_stride))) return rc;
@@ -137,12 +145,13 @@ int h3attn_prep(const h3attn_problem* p,
                           view_range(gamma_q, 1, h, 0, gamma_head_stride, 128, 2),
                           view_range(gamma_k, 1, h, 0, gamma_head_stride, 128, 2),
                           span(pos_thw, (size_t)n * 3 * sizeof(int32_t))};
-    Range outs[4] = {span(q_out, out_b), span(k_out, out_b), {0, 0}, {0, 0}};
-    const int nout = i8 ? 4 : 2;
+    Range outs[5] = {span(q_out, out_b), span(k_out, out_b), {0, 0}, {0, 0}, {0, 0}};
+    const int nout = smooth ? 5 : i8 ? 4 : 2;
     if (i8) {
         outs[2] = span(q_scales, sc_b);
         outs[3] = span(k_scales, sc_b);
     }
+    if (smooth) outs[4] = span(k_mean, (size_t)h * 128 * sizeof(float));
     for (int o = 0; o < nout; ++o) {
         for (const Range& r : ins)
             if (overlap(outs[o], r)) return H3ATTN_E_ALIAS;
@@ -160,8 +169,37 @@ int h3attn_prep(const h3attn_problem* p,
     P.n = (int)n; P.h = (int)h; P.npad = (int)npad_of(p); P.nblk = (int)nblk_of(p);
     P.theta = p->rope_theta; P.eps = p->rms_eps;
     P.sec0 = p->rope_sections[0]; P.sec1 = p->rope_sections[1]; P.sec2 = p->rope_sections[2];
-    if (h3::launch_prep(P, i8, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
+    P.k_mean = k_mean;
+    const hipError_t e = smooth ? h3::launch_prep_ksmooth(P, static_cast<hipStream_t>(stream))
+                                : h3::launch_prep(P, i8, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return H3ATTN_E_HIP;
     return H3ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int h3attn_prep(const h3attn_problem* p,
+                const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                const void* gamma_q, const void* gamma_k, int64_t gamma_head_stride,
+                const int32_t* pos_thw,
+                void* q_out, void* k_out, float* q_scales, float* k_scales,
+                void* stream) {
+    return prep_common(p, q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, gamma_q, gamma_k,
+                       gamma_head_stride, pos_thw, q_out, k_out, q_scales, k_scales, nullptr, false, stream);
+}
+
+int h3attn_prep_ksmooth(const h3attn_problem* p,
+                        const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                        const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                        const void* gamma_q, const void* gamma_k, int64_t gamma_head_stride,
+                        const int32_t* pos_thw,
+                        void* q_out, void* k_out, float* q_scales, float* k_scales,
+                        float* k_mean, void* stream) {
+    return prep_common(p, q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, gamma_q, gamma_k,
+                       gamma_head_stride, pos_thw, q_out, k_out, q_scales, k_scales, k_mean, true, stream);
 }
 
 }  // extern "C"

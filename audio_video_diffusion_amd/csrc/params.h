@@ -13,6 +13,7 @@ struct PrepParams {
     const int32_t* pos;                          // [N][3]
     void* q_out; void* k_out;                    // [H][npad][128] bf16 or int8
     float* q_scales; float* k_scales;            // [H][nblk] (int8 only)
+    float* k_mean;                               // [H][128] K smoothing means (K smoothing only)
     int n, h, npad, nblk;
     float theta, eps;
     int sec0, sec1, sec2;
@@ -49,6 +50,7 @@ struct ScoreParams {
 };
 
 hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream);
+hipError_t launch_prep_ksmooth(const PrepParams& P, hipStream_t stream);
 hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t stream);
 hipError_t launch_prep_v(const PrepVParams& P, hipStream_t stream);
 hipError_t launch_scores_i8(const ScoreParams& P, hipStream_t stream);

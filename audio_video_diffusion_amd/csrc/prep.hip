@@ -18,6 +18,10 @@
 // computed once per token and reused for every head and for both Q and K.
 // The 64-token block is exactly one int8 scale block, so the block absmax is a
 // work-group reduction.
+//
+// With K smoothing (the K-mean step of the same quantised path) the per-head,
+// per-channel mean of K' is subtracted before K is quantised, in three passes
+// (see PrepMode).
 #include "common.h"
 #include "params.h"
 
@@ -106,8 +110,18 @@ __device__ __forceinline__ uint32_t quant4(const float* v, float inv) {
     return w;
 }
 
-template <bool kInt8>
+// kPrepI8Sums and kPrepI8Smooth are the first and last pass of K smoothing:
+// the first writes Q' codes as kPrepI8 does, and for K' the per-block channel
+// sums of its bf16 values (into the K code buffer, used as scratch); after
+// ksum_reduce has turned them into the channel means, the last recomputes K'
+// alone and quantises fl32(k - mean).
+enum PrepMode { kPrepBf16 = 0, kPrepI8 = 1, kPrepI8Sums = 2, kPrepI8Smooth = 3 };
+
+template <int kMode>
 __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
+    constexpr bool kInt8 = kMode != kPrepBf16;
+    constexpr bool kDoQ = kMode != kPrepI8Smooth;     // Q' produced in this pass
+    constexpr bool kQuantK = kMode == kPrepI8 || kMode == kPrepI8Smooth;
     const int tid = threadIdx.x;
     const int row = tid >> 3;            // 0..31
     const int p = tid & 7;               // slot
@@ -144,6 +158,8 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
     load_gamma(0);
 
     __shared__ float red[2][2][4];      // [head parity][q/k][wave]
+    // K smoothing, first pass: one head's bf16 K' block as fp32, [token][channel]
+    __shared__ float ksum_tile[kMode == kPrepI8Sums ? 64 : 1][kMode == kPrepI8Sums ? kHeadDim + 1 : 1];
     const int wave = tid >> 6;
 
     for (int h = 0; h < P.h; ++h) {
@@ -154,8 +170,12 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
             if (valid[t]) {
                 const uint16_t* qr = P.q + (int64_t)tok[t] * P.q_st + (int64_t)h * P.q_sh;
                 const uint16_t* kr = P.k + (int64_t)tok[t] * P.k_st + (int64_t)h * P.k_sh;
-                qa[t] = ld16(qr + 8 * sl.a);
-                qb[t] = ld16(qr + 8 * sl.b);
+                if constexpr (kDoQ) {
+                    qa[t] = ld16(qr + 8 * sl.a);
+                    qb[t] = ld16(qr + 8 * sl.b);
+                } else {
+                    qa[t] = qb[t] = u32x4{0, 0, 0, 0};
+                }
                 ka[t] = ld16(kr + 8 * sl.a);
                 kb[t] = ld16(kr + 8 * sl.b);
             } else {
@@ -167,9 +187,15 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             float xa[8], xb[8];
-            unpack8(qa[t], xa);
-            unpack8(qb[t], xb);
-            norm_rotate(xa, xb, gqa, gqb, cs[t], sn[t], P.eps, oqa[t], oqb[t], rq[t], rq[t] + 8);
+            if constexpr (kDoQ) {
+                unpack8(qa[t], xa);
+                unpack8(qb[t], xb);
+                norm_rotate(xa, xb, gqa, gqb, cs[t], sn[t], P.eps, oqa[t], oqb[t], rq[t], rq[t] + 8);
+            } else {
+                oqa[t] = oqb[t] = u32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int i = 0; i < 16; ++i) rq[t][i] = 0.f;
+            }
             unpack8(ka[t], xa);
             unpack8(kb[t], xb);
             norm_rotate(xa, xb, gka, gkb, cs[t], sn[t], P.eps, oka[t], okb[t], rk[t], rk[t] + 8);
@@ -192,6 +218,41 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
                 st16(ko + r + 8 * sl.b, okb[t]);
             }
         } else {
+            if constexpr (kMode == kPrepI8Smooth) {
+                // quantiser input fl32(k - mean); rows past N stay zero
+                float mu[16];
+                const float* mh = P.k_mean + (int64_t)h * kHeadDim;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    mu[i] = mh[8 * sl.a + i];
+                    mu[8 + i] = mh[8 * sl.b + i];
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    if (valid[t])
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) rk[t][i] = rk[t][i] - mu[i];
+            }
+            if constexpr (kMode == kPrepI8Sums) {
+                // per-channel sum of the block's bf16 K' in token order, one fp32
+                // addition at a time (the order the smoothing mean is defined in)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        ksum_tile[row + 32 * t][8 * sl.a + i] = rk[t][i];
+                        ksum_tile[row + 32 * t][8 * sl.b + i] = rk[t][8 + i];
+                    }
+                __syncthreads();
+                if (tid < kHeadDim && t0 < P.n) {
+                    const int cnt = min(64, P.n - t0);
+                    float acc = 0.f;
+                    for (int i = 0; i < cnt; ++i) acc += ksum_tile[i][tid];
+                    float* sums = static_cast<float*>(P.k_out);
+                    sums[((int64_t)h * P.nblk + blockIdx.x) * kHeadDim + tid] = acc;
+                }
+                __syncthreads();
+            }
             float mq = 0.f, mk = 0.f;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
@@ -221,30 +282,56 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
             const float iq = aq > 0.f ? 127.0f / aq : 0.f;
             const float ik = ak > 0.f ? 127.0f / ak : 0.f;
             if (tid == 0 && t0 < P.n) {
-                P.q_scales[(int64_t)h * P.nblk + blockIdx.x] = sq;
-                P.k_scales[(int64_t)h * P.nblk + blockIdx.x] = sk;
+                if constexpr (kDoQ) P.q_scales[(int64_t)h * P.nblk + blockIdx.x] = sq;
+                if constexpr (kQuantK) P.k_scales[(int64_t)h * P.nblk + blockIdx.x] = sk;
             }
             int8_t* qo = static_cast<int8_t*>(P.q_out);
             int8_t* ko = static_cast<int8_t*>(P.k_out);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int64_t r = (head_base + tok[t]) * kHeadDim;
-                st8(qo + r + 8 * sl.a, u32x2{quant4(rq[t], iq), quant4(rq[t] + 4, iq)});
-                st8(qo + r + 8 * sl.b, u32x2{quant4(rq[t] + 8, iq), quant4(rq[t] + 12, iq)});
-                st8(ko + r + 8 * sl.a, u32x2{quant4(rk[t], ik), quant4(rk[t] + 4, ik)});
-                st8(ko + r + 8 * sl.b, u32x2{quant4(rk[t] + 8, ik), quant4(rk[t] + 12, ik)});
+                if constexpr (kDoQ) {
+                    st8(qo + r + 8 * sl.a, u32x2{quant4(rq[t], iq), quant4(rq[t] + 4, iq)});
+                    st8(qo + r + 8 * sl.b, u32x2{quant4(rq[t] + 8, iq), quant4(rq[t] + 12, iq)});
+                }
+                if constexpr (kQuantK) {
+                    st8(ko + r + 8 * sl.a, u32x2{quant4(rk[t], ik), quant4(rk[t] + 4, ik)});
+                    st8(ko + r + 8 * sl.b, u32x2{quant4(rk[t] + 8, ik), quant4(rk[t] + 12, ik)});
+                }
             }
         }
     }
+}
+
+// K smoothing, middle pass: mean[h][c] = (sum over blocks in order of the
+// block sums) / N, one fp32 addition at a time; one thread per (head, channel)
+__global__ void __launch_bounds__(256) ksum_reduce(const float* sums, float* mean, int h, int nblk, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= h * kHeadDim) return;
+    const int head = i / kHeadDim, c = i % kHeadDim;
+    const float* s = sums + (int64_t)head * nblk * kHeadDim + c;
+    float acc = 0.f;
+    for (int b = 0; b < nblk; ++b) acc += s[(int64_t)b * kHeadDim];
+    mean[i] = acc / (float)n;       // IEEE division (no fast-math in this build)
 }
 
 hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
     dim3 grid(P.npad / 64), block(256);
     if (int8)
-        hipLaunchKernelGGL(prep_kernel<true>, grid, block, 0, stream, P);
+        hipLaunchKernelGGL(prep_kernel<kPrepI8>, grid, block, 0, stream, P);
     else
-        hipLaunchKernelGGL(prep_kernel<false>, grid, block, 0, stream, P);
+        hipLaunchKernelGGL(prep_kernel<kPrepBf16>, grid, block, 0, stream, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_ksmooth(const PrepParams& P, hipStream_t stream) {
+    (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
+    dim3 grid(P.npad / 64), block(256);
+    hipLaunchKernelGGL(prep_kernel<kPrepI8Sums>, grid, block, 0, stream, P);
+    hipLaunchKernelGGL(ksum_reduce, dim3((P.h * kHeadDim + 255) / 256), block, 0, stream,
+                       static_cast<const float*>(P.k_out), P.k_mean, P.h, P.nblk, P.n);
+    hipLaunchKernelGGL(prep_kernel<kPrepI8Smooth>, grid, block, 0, stream, P);
     return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@ fallback: if the library is not built, importing the binding raises.
 The calls mirror ``include/h3attn.h``:
 
 * :func:`prep`      - Q/K RMSNorm + 3-axis split-half RoPE -> head-major Q'/K'
+* :func:`prep_ksmooth` - :func:`prep` in the int8 format with K smoothing
 * :func:`forward`   - softmax(Q' K'^T * scale) V over the packed sequence
 * :func:`prep_v_fp8` - V -> E4M3 codes (d-major 64-key tiles) + fp32 channel scales
 * :func:`forward_fp8v` - :func:`forward` with the P V product on FP8 matrix cores
@@ -22,7 +23,7 @@ LIB_PATH = os.path.join(PKG, "libh3attn.so")
 
 QK_BF16 = 0
 QK_I8_BLK64 = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_UNSUPPORTED", -4: "E_ALIGN",
           -5: "E_ALIAS", -6: "E_HIP"}
@@ -87,6 +88,8 @@ def _load():
         "h3attn_prep": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, i64, vp, vp, i64, vp,
                                        vp, vp, vp, vp, vp]),
         "h3attn_forward": (ctypes.c_int, [pp, vp, vp, vp, vp, vp, i64, i64, vp, i64, i64, f32, vp]),
+        "h3attn_prep_ksmooth": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, i64, vp, vp, i64, vp,
+                                               vp, vp, vp, vp, vp, vp]),
         "h3attn_prep_v_fp8": (ctypes.c_int, [pp, vp, i64, i64, vp, vp, vp]),
         "h3attn_forward_fp8v": (ctypes.c_int, [pp, vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, vp]),
         "h3attn_debug_scores_i32": (ctypes.c_int, [pp, vp, vp, i32, i32, i32, i32, i32, vp, vp]),
@@ -173,6 +176,21 @@ def prep(p: Problem, q, k, gamma_q, gamma_k, pos, q_out, k_out, q_scales=None, k
                           _stream(stream))
     if rc:
         raise H3AttnError(rc, "h3attn_prep")
+
+
+def prep_ksmooth(p: Problem, q, k, gamma_q, gamma_k, pos, q_out, k_out, q_scales, k_scales, k_mean,
+                 stream=None):
+    """``h3attn_prep_ksmooth``: int8 prep with K smoothing; ``k_mean`` fp32 [H, 128] receives the means."""
+    qp, qst, qsh = _nhd(q, "q")
+    kp, kst, ksh = _nhd(k, "k")
+    if gamma_q.shape != gamma_k.shape or gamma_q.stride() != gamma_k.stride():
+        raise ValueError("gamma_q and gamma_k must have the same shape and strides")
+    gsh = gamma_q.stride(0) if gamma_q.dim() == 2 else 0
+    rc = _lib.h3attn_prep_ksmooth(ctypes.byref(p), qp, qst, qsh, kp, kst, ksh, _ptr(gamma_q), _ptr(gamma_k),
+                                  gsh, _ptr(pos), _ptr(q_out), _ptr(k_out), _ptr(q_scales), _ptr(k_scales),
+                                  _ptr(k_mean), _stream(stream))
+    if rc:
+        raise H3AttnError(rc, "h3attn_prep_ksmooth")
 
 
 def forward(p: Problem, q_prep, k_prep, v, o, softmax_scale: float, q_scales=None, k_scales=None,

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 3
+#define H3ATTN_ABI_VERSION 4
 
 typedef enum {
     H3ATTN_OK = 0,
@@ -141,6 +141,35 @@ int h3attn_prep(const h3attn_problem* p,
                 const int32_t* pos_thw,
                 void* q_out, void* k_out, float* q_scales, float* k_scales,
                 void* stream);
+
+/*
+ * h3attn_prep_ksmooth - h3attn_prep in the int8 format with K smoothing: the
+ * per-head, per-channel mean of K' over all tokens is subtracted before K' is
+ * quantised, the K-mean step of the quantised path ("H3 Runtime Current
+ * State", Owned Performance Kernels: K mean, then K quantization).  Every
+ * score of a query row shifts by the same q . mean, so the attention is
+ * unchanged up to quantisation, while the int8 K codes resolve the spread
+ * around the mean instead of a common offset.
+ *   mean[h][c] = S / N in fp32, where S adds, in block order, the fp32 sums
+ *                of each 64-token block taken in token order (one rounding
+ *                per addition) over the bf16-rounded K'[n,h,c];
+ *   K codes/scales = the int8 quantiser of h3attn_prep applied to
+ *                fl32(K'[n,h,c] - mean[h][c]) (rows n >= N stay zero).
+ * Q' codes/scales are exactly those of h3attn_prep.  Feed the outputs to
+ * h3attn_forward / h3attn_forward_fp8v as int8 Q'/K' (mean is not needed).
+ * k_mean: device fp32 [H][128], 4-byte aligned, written; must not overlap the
+ *         other arguments.  k_out also serves as scratch during the call.
+ * Requires qk_format == H3ATTN_QK_I8_BLK64 (E_UNSUPPORTED otherwise).  Three
+ * kernels on `stream`; nothing is allocated.  Other arguments and errors: as
+ * for h3attn_prep.
+ */
+int h3attn_prep_ksmooth(const h3attn_problem* p,
+                        const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                        const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                        const void* gamma_q, const void* gamma_k, int64_t gamma_head_stride,
+                        const int32_t* pos_thw,
+                        void* q_out, void* k_out, float* q_scales, float* k_scales,
+                        float* k_mean, void* stream);
 
 /*
  * h3attn_forward - non-causal attention over the whole packed sequence.

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 3
+    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 4
     for s in (0, -1, -2, -3, -4, -5, -6, 7):
         assert A.lib.h3attn_status_string(s)
 
@@ -111,6 +111,23 @@ def test_prep_pointer_and_alignment_checks():
     p8 = A.problem(1000, 3, A.QK_I8_BLK64)
     assert prep(p8) == -1                     # scales missing in int8 format
     assert prep(p8, qs=K, ks=K + 4096, qo=J + 3) == -4
+
+
+def prep_ks(p, q=F, qst=384, qsh=128, k=G, kst=384, ksh=128, gq=H, gk=H + 256, gsh=0, pos=I,
+            qo=J, ko=J + (1 << 32), qs=K, ks=K + 4096, km=K + 8192):
+    return A.lib.h3attn_prep_ksmooth(ctypes.byref(p), q, qst, qsh, k, kst, ksh, gq, gk, gsh, pos,
+                                     qo, ko, qs, ks, km, None)
+
+
+def test_prep_ksmooth_checks():
+    p8 = A.problem(1000, 3, A.QK_I8_BLK64)
+    assert prep_ks(A.problem(1000, 3)) == -3             # bf16 format: nothing to smooth
+    assert prep_ks(p8, km=None) == -1
+    assert prep_ks(p8, km=K + 8194) == -4
+    assert prep_ks(p8, km=K + 16) == -5                  # mean over the q scales
+    assert prep_ks(p8, km=J + 64) == -5                  # mean inside q_out
+    assert prep_ks(p8, qs=None) == -1
+    assert prep_ks(p8, q=None) == -1
 
 
 def test_prep_alias_checks():
