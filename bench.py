@@ -160,11 +160,12 @@ def mfma_sustained(A, launches=6, blocks=2048, iters=6000):
     return statistics.median(rates[2:])
 
 
-def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=None, vfp8=None):
+def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=None, vfp8=None, kmean=None):
     """HIP-event times (ms) of prep and forward over `steps` calls after `warmup`.
 
     With ``vfp8 = (codes, scales)`` each step also stages V as E4M3 (timed on
     its own) and runs the FP8 P V forward; the third list holds those times.
+    With ``kmean`` (fp32 [H, 128]) the int8 prep applies K smoothing.
     """
     import torch
     q, k, v = dev["q"], dev["k"], dev["v"]
@@ -175,7 +176,10 @@ def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=No
     for i in range(warmup + steps):
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record()
-        A.prep(p, q, k, dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
+        if kmean is None:
+            A.prep(p, q, k, dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
+        else:
+            A.prep_ksmooth(p, q, k, dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks, kmean)
         e1.record()
         if vfp8 is not None:
             A.prep_v_fp8(p, v, vfp8[0], vfp8[1])
@@ -196,7 +200,8 @@ def sweep(A, W, headline_dev, steps=3, warmup=1):
     """Forward throughput of every other workload: the remaining configurations,
     the headline's per-GPU head shards, the pages' block-24 shape, and the FP8
     P V variants (V staged as E4M3) on the headline, the 243-frame int8
-    workload and the block-24 shape."""
+    workload and the block-24 shape.  The int8 Q/K + FP8 P V rows are the whole
+    quantised path of the pages, K smoothing included in their prep."""
     import statistics
     import torch
     scale = 1.0 / math.sqrt(128.0)
@@ -225,13 +230,16 @@ def sweep(A, W, headline_dev, steps=3, warmup=1):
         p = A.problem(wl.n_tokens, wl.heads, fmt)
         q_out, k_out, qs, ks = A.alloc_prepped(p)
         vfp8 = A.alloc_v_fp8(p) if fp8v else None
+        ksm = int8 and fp8v
+        kmean = torch.empty((wl.heads, 128), dtype=torch.float32, device="cuda") if ksm else None
         o = torch.empty((wl.n_tokens, wl.heads, 128), dtype=torch.bfloat16, device="cuda")
         prep_ms, fwd_ms, prepv_ms = time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup,
-                                              shard_heads, vfp8)
+                                              shard_heads, vfp8, kmean)
         med = statistics.median(fwd_ms)
         tf = wl.flops / (med * 1e-3) / 1e12
         row = {"workload": wl.name, "n_tokens": wl.n_tokens, "heads": wl.heads,
-               "qk": "int8" if int8 else "bf16", "pv": "fp8" if fp8v else "bf16", "steps": steps,
+               "qk": "int8" if int8 else "bf16", "pv": "fp8" if fp8v else "bf16", "k_smoothing": ksm,
+               "steps": steps,
                "forward_ms": {"median": round(med, 4), "min": round(min(fwd_ms), 4), "max": round(max(fwd_ms), 4)},
                "prep_ms": round(statistics.median(prep_ms), 4),
                "forward_tflops": round(tf, 2), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
@@ -244,7 +252,7 @@ def sweep(A, W, headline_dev, steps=3, warmup=1):
             ideal_ms = (wl.flops / 2 / (qk_peak * 1e12) + wl.flops / 2 / (pv_peak * 1e12)) * 1e3
             row["pct_mixed_peak"] = round(100 * ideal_ms / med, 2)
         rows.append(row)
-        del q_out, k_out, qs, ks, o, vfp8
+        del q_out, k_out, qs, ks, o, vfp8, kmean
         torch.cuda.empty_cache()
     return rows
 
