@@ -142,6 +142,15 @@ __device__ __forceinline__ void mfma_s(f32x16& d, const bf16x8& a, const bf16x8&
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
+// The int8 form of mfma_s: int32 scores in arch VGPRs (the softmax converts
+// them there), Q' codes in AGPRs.
+__device__ __forceinline__ void mfma_s_i8(i32x16& d, const i32x4& a, const i32x4& b, bool first) {
+    if (first)
+        asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+    else
+        asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+
 __device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const i32x4 (&q)[2][4], i32x16 (&S)[2][2],
                                         int n32, int hh) {
 #pragma unroll
@@ -397,12 +406,14 @@ fwd8_kernel(FwdParams P) {
                 for (int t = 0; t < 4; ++t)
                     a[kb][t] = *reinterpret_cast<const i32x4*>(kb_ + rho * 128 + (((2 * t + hh) ^ (rho & 7)) * 16));
             }
-            i32x16 Si[2] = {i32x16{}, i32x16{}};
+            i32x16 Si[2];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                Si[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0][t], q[t], Si[0], 0, 0, 0);
-                Si[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[1][t], q[t], Si[1], 0, 0, 0);
+                mfma_s_i8(Si[0], a[0][t], q[t], t == 0);
+                mfma_s_i8(Si[1], a[1][t], q[t], t == 0);
             }
+            // wait states before the VALU reads the matrix core's results
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(Si[0]), "+v"(Si[1]));
             // |S| <= 127 * 127 * 128 < 2^24: exact in fp32
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
