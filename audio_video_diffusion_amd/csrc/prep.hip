@@ -311,7 +311,16 @@ __global__ void __launch_bounds__(256) ksum_reduce(const float* sums, float* mea
     const int head = i / kHeadDim, c = i % kHeadDim;
     const float* s = sums + (int64_t)head * nblk * kHeadDim + c;
     float acc = 0.f;
-    for (int b = 0; b < nblk; ++b) acc += s[(int64_t)b * kHeadDim];
+    int b = 0;
+    // loads run ahead in groups of 16; the additions stay in block order
+    for (; b + 16 <= nblk; b += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = s[(int64_t)(b + u) * kHeadDim];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc += v[u];
+    }
+    for (; b < nblk; ++b) acc += s[(int64_t)b * kHeadDim];
     mean[i] = acc / (float)n;       // IEEE division (no fast-math in this build)
 }
 
