@@ -39,9 +39,9 @@ PEAK_HBM_GBS = 8000.0
 # csrc/forward.hip no longer hashes to `source_sha256`, traffic is null.
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
-    "source_sha256": "52e6d42ef0b64f90db329c63ecede6d9610354266e2244e4fa3c5688786eeb71",
-    "fetch_kib": 13332859.7, "fetch_scale": 2.0,
-    "write_kib": 817518.3, "write_scale": 1.0,
+    "source_sha256": "e2622cd31e61e9d17a6543c35d07fc0552a9126872b14979ff83b3da4323acc7",
+    "fetch_kib": 13332855.8, "fetch_scale": 2.0,
+    "write_kib": 809104.5, "write_scale": 1.0,
 }
 
 
