@@ -84,6 +84,18 @@ def test_problem_validation(kw, field, val, code):
     assert fwd(p) == code
 
 
+def test_size_limits():
+    # the largest accepted shapes keep every 32-bit index in range; one past is rejected
+    assert A.padded_tokens(A.problem(1 << 30, 1)) == 1 << 30
+    assert fwd(A.problem((1 << 30) + 1, 1)) == -2
+    assert prep(A.problem((1 << 30) + 1, 1)) == -2
+    assert A.prepped_qk_bytes(A.problem(1 << 30, 1 << 10)) == (1 << 30) * (1 << 10) * 128 * 2
+    assert fwd(A.problem(1 << 30, (1 << 10) + 1)) == -2      # H * N_pad above 2^40
+    # the largest accepted V token stride passes its check and fails only at the later
+    # scale check (so nothing is ever launched on these fake pointers)
+    assert fwd(A.problem(1000, 3), vst=(1 << 24), scale=0.0) == -2
+
+
 def test_section_validation():
     p = A.problem(1000, 3, sections=(32, 48, 32))
     assert prep(p) == -2                       # does not sum to 128
