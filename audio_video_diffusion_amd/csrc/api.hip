@@ -56,6 +56,13 @@ int check_problem(const h3attn_problem* p) {
 }
 
 int64_t npad_of(const h3attn_problem* p) { return ((int64_t)p->n_tokens + 255) / 256 * 256; }
+
+// theta^(-2/s) of RoPE section a in fp64: the kernels take the inverse
+// frequencies theta^(-2j/s) as its powers (1 for an empty section).
+double rope_ratio(const h3attn_problem* p, int a) {
+    const int s = p->rope_sections[a];
+    return s > 0 ? pow((double)p->rope_theta, -2.0 / (double)s) : 1.0;
+}
 int64_t nblk_of(const h3attn_problem* p) { return ((int64_t)p->n_tokens + 63) / 64; }
 
 // strides of an input view: non-negative multiples of 8 elements
@@ -114,20 +121,28 @@ size_t h3attn_v_scales_bytes(const h3attn_problem* p) {
 
 namespace {
 
-// Shared by h3attn_prep and h3attn_prep_ksmooth (int8 with K smoothing).
+// Shared by h3attn_prep, h3attn_prep_ksmooth (int8 with K smoothing) and
+// h3attn_prep_k (bf16 K' alone: q, gamma_q and q_out are unused and NULL).
 int prep_common(const h3attn_problem* p,
                 const void* q, int64_t q_stride_tok, int64_t q_stride_head,
                 const void* k, int64_t k_stride_tok, int64_t k_stride_head,
                 const void* gamma_q, const void* gamma_k, int64_t gamma_head_stride,
                 const int32_t* pos_thw,
                 void* q_out, void* k_out, float* q_scales, float* k_scales,
-                float* k_mean, bool smooth, void* stream) {
+                float* k_mean, bool smooth, bool k_only, void* stream) {
     int rc = check_problem(p);
     if (rc) return rc;
     const bool i8 = p->qk_format == H3ATTN_QK_I8_BLK64;
     if (smooth && !i8) return H3ATTN_E_UNSUPPORTED;
+    if (k_only && i8) return H3ATTN_E_UNSUPPORTED;
     if (smooth && !k_mean) return H3ATTN_E_NULL;
     if (smooth && !aligned(k_mean, 4)) return H3ATTN_E_ALIGN;
+    if (k_only) {
+        // placeholders for the absent Q side: the same buffers as K, never read or written
+        q = k; q_stride_tok = k_stride_tok; q_stride_head = k_stride_head;
+        gamma_q = gamma_k;
+        q_out = k_out;
+    }
     if ((rc = check_in_view(q, q_stride_tok, q_stride_head))) return rc;
     if ((rc = check_in_view(k, k_stride_tok, k_stride_head))) return rc;
     if ((rc = check_in_view(gamma_q, 0, gamma_head_stride))) return rc;
@@ -146,7 +161,11 @@ int prep_common(const h3attn_problem* p,
                           view_range(gamma_k, 1, h, 0, gamma_head_stride, 128, 2),
                           span(pos_thw, (size_t)n * 3 * sizeof(int32_t))};
     Range outs[5] = {span(q_out, out_b), span(k_out, out_b), {0, 0}, {0, 0}, {0, 0}};
-    const int nout = smooth ? 5 : i8 ? 4 : 2;
+    int nout = smooth ? 5 : i8 ? 4 : 2;
+    if (k_only) {
+        outs[0] = outs[1];
+        nout = 1;
+    }
     if (i8) {
         outs[2] = span(q_scales, sc_b);
         outs[3] = span(k_scales, sc_b);
@@ -167,11 +186,16 @@ int prep_common(const h3attn_problem* p,
     P.pos = pos_thw;
     P.q_out = q_out; P.k_out = k_out; P.q_scales = q_scales; P.k_scales = k_scales;
     P.n = (int)n; P.h = (int)h; P.npad = (int)npad_of(p); P.nblk = (int)nblk_of(p);
-    P.theta = p->rope_theta; P.eps = p->rms_eps;
+    P.eps = p->rms_eps;
+    P.rho0 = rope_ratio(p, 0); P.rho1 = rope_ratio(p, 1); P.rho2 = rope_ratio(p, 2);
     P.sec0 = p->rope_sections[0]; P.sec1 = p->rope_sections[1]; P.sec2 = p->rope_sections[2];
     P.k_mean = k_mean;
-    const hipError_t e = smooth ? h3::launch_prep_ksmooth(P, static_cast<hipStream_t>(stream))
-                                : h3::launch_prep(P, i8, static_cast<hipStream_t>(stream));
+    if (k_only) {
+        P.q = nullptr; P.gq = nullptr; P.q_out = nullptr;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = smooth ? h3::launch_prep_ksmooth(P, st) : k_only ? h3::launch_prep_k(P, st)
+                                                                          : h3::launch_prep(P, i8, st);
     if (e != hipSuccess) return H3ATTN_E_HIP;
     return H3ATTN_OK;
 }
@@ -188,7 +212,14 @@ int h3attn_prep(const h3attn_problem* p,
                 void* q_out, void* k_out, float* q_scales, float* k_scales,
                 void* stream) {
     return prep_common(p, q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, gamma_q, gamma_k,
-                       gamma_head_stride, pos_thw, q_out, k_out, q_scales, k_scales, nullptr, false, stream);
+                       gamma_head_stride, pos_thw, q_out, k_out, q_scales, k_scales, nullptr, false, false, stream);
+}
+
+int h3attn_prep_k(const h3attn_problem* p, const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                  const void* gamma_k, int64_t gamma_head_stride, const int32_t* pos_thw, void* k_out,
+                  void* stream) {
+    return prep_common(p, nullptr, 0, 0, k, k_stride_tok, k_stride_head, nullptr, gamma_k, gamma_head_stride,
+                       pos_thw, nullptr, k_out, nullptr, nullptr, nullptr, false, true, stream);
 }
 
 int h3attn_prep_ksmooth(const h3attn_problem* p,
@@ -199,21 +230,40 @@ int h3attn_prep_ksmooth(const h3attn_problem* p,
                         void* q_out, void* k_out, float* q_scales, float* k_scales,
                         float* k_mean, void* stream) {
     return prep_common(p, q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, gamma_q, gamma_k,
-                       gamma_head_stride, pos_thw, q_out, k_out, q_scales, k_scales, k_mean, true, stream);
+                       gamma_head_stride, pos_thw, q_out, k_out, q_scales, k_scales, k_mean, true, false, stream);
 }
 
 }  // extern "C"
 
 namespace {
 
-// Shared by h3attn_forward (bf16 V view) and h3attn_forward_fp8v (staged E4M3 V).
+// Raw-Q inputs of h3attn_forward_fused_q.
+struct RawQ {
+    const void* q;
+    int64_t st, sh;
+    const void* gamma;
+    int64_t g_sh;
+    const int32_t* pos;
+};
+
+// Shared by h3attn_forward (bf16 V view), h3attn_forward_fp8v (staged E4M3 V)
+// and h3attn_forward_fused_q (raw Q in place of q_prep, bf16 only).
 int forward_common(const h3attn_problem* p, const void* q_prep, const void* k_prep,
                    const float* q_scales, const float* k_scales, bool fp8v, const void* v,
                    int64_t v_stride_tok, int64_t v_stride_head, const float* v_scales, void* o,
-                   int64_t o_stride_tok, int64_t o_stride_head, float softmax_scale, void* stream) {
+                   int64_t o_stride_tok, int64_t o_stride_head, float softmax_scale, const RawQ* rq,
+                   void* stream) {
     int rc = check_problem(p);
     if (rc) return rc;
     const bool i8 = p->qk_format == H3ATTN_QK_I8_BLK64;
+    if (rq) {
+        if (i8 || fp8v) return H3ATTN_E_UNSUPPORTED;
+        if ((rc = check_in_view(rq->q, rq->st, rq->sh))) return rc;
+        if ((rc = check_in_view(rq->gamma, 0, rq->g_sh))) return rc;
+        if (!rq->pos) return H3ATTN_E_NULL;
+        if (!aligned(rq->pos, 4)) return H3ATTN_E_ALIGN;
+        q_prep = k_prep;     // placeholder for the checks below; never read
+    }
     if (!q_prep || !k_prep) return H3ATTN_E_NULL;
     if (!aligned(q_prep, 16) || !aligned(k_prep, 16)) return H3ATTN_E_ALIGN;
     if (i8 && (!q_scales || !k_scales)) return H3ATTN_E_NULL;
@@ -245,6 +295,10 @@ int forward_common(const h3attn_problem* p, const void* q_prep, const void* k_pr
     if (i8 && (overlap(orng, span(q_scales, sc_b)) || overlap(orng, span(k_scales, sc_b))))
         return H3ATTN_E_ALIAS;
     if (fp8v && overlap(orng, span(v_scales, h3attn_v_scales_bytes(p)))) return H3ATTN_E_ALIAS;
+    if (rq && (overlap(orng, view_range(rq->q, n, h, rq->st, rq->sh, 128, 2)) ||
+               overlap(orng, view_range(rq->gamma, 1, h, 0, rq->g_sh, 128, 2)) ||
+               overlap(orng, span(rq->pos, (size_t)n * 3 * sizeof(int32_t)))))
+        return H3ATTN_E_ALIAS;
 
     h3::FwdParams P{};
     P.q = q_prep; P.k = k_prep; P.qs = q_scales; P.ks = k_scales;
@@ -258,6 +312,17 @@ int forward_common(const h3attn_problem* p, const void* q_prep, const void* k_pr
     P.total = (int)total;
     P.per_xcd = (int)((total + 7) / 8);
     P.c = (float)((double)softmax_scale * 1.4426950408889634);
+    if (rq) {
+        P.q = nullptr;
+        P.qraw = static_cast<const uint16_t*>(rq->q); P.q_st = rq->st; P.q_sh = rq->sh;
+        P.gq = static_cast<const uint16_t*>(rq->gamma); P.g_sh = rq->g_sh;
+        P.pos = rq->pos;
+        P.eps = p->rms_eps;
+        P.rho0 = rope_ratio(p, 0); P.rho1 = rope_ratio(p, 1); P.rho2 = rope_ratio(p, 2);
+        P.sec0 = p->rope_sections[0]; P.sec1 = p->rope_sections[1]; P.sec2 = p->rope_sections[2];
+        if (h3::launch_forward_fused_q(P, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
+        return H3ATTN_OK;
+    }
     if (h3::launch_forward(P, i8, fp8v, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
     return H3ATTN_OK;
 }
@@ -273,7 +338,19 @@ int h3attn_forward(const h3attn_problem* p,
                    void* o, int64_t o_stride_tok, int64_t o_stride_head,
                    float softmax_scale, void* stream) {
     return forward_common(p, q_prep, k_prep, q_scales, k_scales, false, v, v_stride_tok, v_stride_head,
-                          nullptr, o, o_stride_tok, o_stride_head, softmax_scale, stream);
+                          nullptr, o, o_stride_tok, o_stride_head, softmax_scale, nullptr, stream);
+}
+
+int h3attn_forward_fused_q(const h3attn_problem* p,
+                           const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                           const void* gamma_q, int64_t gamma_head_stride, const int32_t* pos_thw,
+                           const void* k_prep,
+                           const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                           void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                           float softmax_scale, void* stream) {
+    const RawQ rq{q, q_stride_tok, q_stride_head, gamma_q, gamma_head_stride, pos_thw};
+    return forward_common(p, nullptr, k_prep, nullptr, nullptr, false, v, v_stride_tok, v_stride_head, nullptr,
+                          o, o_stride_tok, o_stride_head, softmax_scale, &rq, stream);
 }
 
 int h3attn_forward_fp8v(const h3attn_problem* p,
@@ -283,7 +360,7 @@ int h3attn_forward_fp8v(const h3attn_problem* p,
                         void* o, int64_t o_stride_tok, int64_t o_stride_head,
                         float softmax_scale, void* stream) {
     return forward_common(p, q_prep, k_prep, q_scales, k_scales, true, v_codes, 0, 0, v_scales, o,
-                          o_stride_tok, o_stride_head, softmax_scale, stream);
+                          o_stride_tok, o_stride_head, softmax_scale, nullptr, stream);
 }
 
 int h3attn_prep_v_fp8(const h3attn_problem* p, const void* v, int64_t v_stride_tok, int64_t v_stride_head,

@@ -48,6 +48,7 @@
 
 #include "common.h"
 #include "params.h"
+#include "rope_norm.h"
 
 namespace h3 {
 
@@ -307,9 +308,13 @@ struct DmaOffsets8 {
 // factor multiplies numerator and denominator alike and cancels.
 constexpr float kPLog2Fp8 = 0.8f;
 
-template <bool kInt8, bool kFp8V>
+// kFuseQ (bf16 only): Q' is not read from memory but computed in the prologue
+// from raw Q with the prep kernel's own per-row routine (rope_norm.h), so the
+// result is bit-identical to prep + forward.
+template <bool kInt8, bool kFp8V, bool kFuseQ = false>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd8_kernel(FwdParams P) {
+    static_assert(!(kFuseQ && kInt8), "the fused Q prologue produces bf16 Q'");
     using D = DmaOffsets8<kInt8, kFp8V>;
     constexpr int kKTileB = kBN * D::kRowB;        // 16 KB (bf16) or 8 KB (int8)
     constexpr int kVTileB = kBN * (kFp8V ? 128 : 256);   // 8 KB (E4M3) or 16 KB (bf16)
@@ -343,9 +348,36 @@ fwd8_kernel(FwdParams P) {
     using QOp = typename std::conditional<kInt8, i32x4, bf16x8>::type;
     constexpr int kSteps = kInt8 ? 4 : 8;          // d-steps of 32 (int8) or 16 (bf16)
     QOp q[kSteps];
+    if constexpr (!kFuseQ) {
 #pragma unroll
-    for (int t = 0; t < kSteps; ++t)
-        q[t] = __builtin_bit_cast(QOp, ld16(qhead + (int64_t)(q0 + n32) * D::kRowB + 32 * t + 16 * hh));
+        for (int t = 0; t < kSteps; ++t)
+            q[t] = __builtin_bit_cast(QOp, ld16(qhead + (int64_t)(q0 + n32) * D::kRowB + 32 * t + 16 * hh));
+    }
+    // Fused Q: thread (r = tid / 8, slot tid % 8) prepares rows r + 64 ps,
+    // ps = 0..3, of the work-group's 256; its raw Q chunks, positions, gamma
+    // and the slot's RoPE frequencies are loaded here, before the K'/V stream
+    // starts (see the wait below).
+    const Slot fsl = slot_of(tid & 7, P.sec0, P.sec1, P.sec2);
+    u32x4 fqa[4], fqb[4], fga, fgb;
+    double fpv[4], ffreq[8];
+    if constexpr (kFuseQ) {
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps) {
+            const int tok = qt * kBM + 64 * ps + (tid >> 3);
+            if (tok < n) {
+                const uint16_t* qr = P.qraw + (int64_t)tok * P.q_st + (int64_t)head * P.q_sh;
+                fqa[ps] = ld16(qr + 8 * fsl.a);
+                fqb[ps] = ld16(qr + 8 * fsl.b);
+                fpv[ps] = (double)P.pos[(int64_t)tok * 3 + fsl.axis];
+            } else {
+                fqa[ps] = fqb[ps] = u32x4{0, 0, 0, 0};
+                fpv[ps] = 0.0;
+            }
+        }
+        fga = ld16(P.gq + (int64_t)head * P.g_sh + 8 * fsl.a);
+        fgb = ld16(P.gq + (int64_t)head * P.g_sh + 8 * fsl.b);
+        rope_freqs(fsl, P.rho0, P.rho1, P.rho2, ffreq);
+    }
     float qscale = 1.f;
     if constexpr (kInt8) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
     // K block scales through the constant address space: one scalar load per
@@ -557,6 +589,45 @@ fwd8_kernel(FwdParams P) {
     fetch(0);
     fetch(1);
     fetch(2);
+    if constexpr (kFuseQ) {
+        // Q' of the work-group's 256 rows, computed while tiles 0..2 stream
+        // in, in two halves of 128 rows staged through LDS stage 3 (K' part:
+        // rows 0..63 of the half, V part: rows 64..127), 16-byte chunks
+        // XOR-swizzled by the row; waves 4h..4h+3 take their MFMA operands
+        // from half h.
+        float ga[8], gb[8];
+        unpack8(fga, ga);
+        unpack8(fgb, gb);
+        const int r = tid >> 3;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int ps = 2 * half + s;
+                float cs[8], sn[8], xa[8], xb[8], ra[8], rb[8];
+                rope_angles(fpv[ps], ffreq, cs, sn);
+                unpack8(fqa[ps], xa);
+                unpack8(fqb[ps], xb);
+                u32x4 oa, ob;
+                norm_rotate(xa, xb, ga, gb, cs, sn, P.eps, oa, ob, ra, rb);
+                if (qt * kBM + 64 * ps + r >= n) oa = ob = u32x4{0, 0, 0, 0};
+                uint8_t* st = (s == 0 ? kbuf(3) : vbuf(3)) + r * 256;
+                *reinterpret_cast<u32x4*>(st + ((fsl.a ^ (r & 15)) * 16)) = oa;
+                *reinterpret_cast<u32x4*>(st + ((fsl.b ^ (r & 15)) * 16)) = ob;
+            }
+            __syncthreads();
+            if ((wave >> 2) == half) {
+                const int row = (wave & 3) * 32 + n32;            // row of the half
+                const uint8_t* src = ((wave & 3) < 2 ? kbuf(3) : vbuf(3)) + (row & 63) * 256;
+#pragma unroll
+                for (int t = 0; t < kSteps; ++t)
+                    q[t] = *reinterpret_cast<const QOp*>(src + (((2 * t + hh) ^ (row & 15)) * 16));
+            }
+            // the staging reads are complete before stage 3 is written again
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+    }
     wait_vmem_upto<2 * kDma8>();
     __syncthreads();
     for (int j = 0; j < last; ++j) tile(j, false);
@@ -599,6 +670,12 @@ hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t 
         hipLaunchKernelGGL((fwd8_kernel<false, true>), grid, block, 0, stream, P);
     else
         hipLaunchKernelGGL((fwd8_kernel<false, false>), grid, block, 0, stream, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_forward_fused_q(const FwdParams& P, hipStream_t stream) {
+    (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
+    hipLaunchKernelGGL((fwd8_kernel<false, false, true>), dim3(kXcds * P.per_xcd), dim3(512), 0, stream, P);
     return hipGetLastError();
 }
 

@@ -15,7 +15,8 @@ struct PrepParams {
     float* q_scales; float* k_scales;            // [H][nblk] (int8 only)
     float* k_mean;                               // [H][128] K smoothing means (K smoothing only)
     int n, h, npad, nblk;
-    float theta, eps;
+    float eps;
+    double rho0, rho1, rho2;   // theta^(-2/s) of the t, h and w sections (fp64, from the host)
     int sec0, sec1, sec2;
 };
 
@@ -33,6 +34,13 @@ struct FwdParams {
     const float* ks;
     const uint16_t* v; int64_t v_st, v_sh;      // bf16 V view, or E4M3 V tiles (fp8v)
     const float* vs;                             // [H][128] V channel scales (fp8v only)
+    // fused-Q forward only: raw Q (bf16 NHD view), gamma_q, positions and RoPE / RMSNorm parameters
+    const uint16_t* qraw; int64_t q_st, q_sh;
+    const uint16_t* gq; int64_t g_sh;
+    const int32_t* pos;
+    float eps;
+    double rho0, rho1, rho2;   // theta^(-2/s) of the t, h and w sections (fp64, from the host)
+    int sec0, sec1, sec2;
     uint16_t* o; int64_t o_st, o_sh;
     int n, h, npad, nblk;
     int qtiles;             // ceil(N / 256)
@@ -50,8 +58,11 @@ struct ScoreParams {
 };
 
 hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream);
+hipError_t launch_prep_k(const PrepParams& P, hipStream_t stream);
 hipError_t launch_prep_ksmooth(const PrepParams& P, hipStream_t stream);
 hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t stream);
+// bf16 Q'/K', V through its view, Q' computed from raw Q in the prologue
+hipError_t launch_forward_fused_q(const FwdParams& P, hipStream_t stream);
 hipError_t launch_prep_v(const PrepVParams& P, hipStream_t stream);
 hipError_t launch_scores_i8(const ScoreParams& P, hipStream_t stream);
 hipError_t launch_mfma_calib(float* out, int blocks, int iters, hipStream_t stream);

@@ -24,80 +24,10 @@
 // (see PrepMode).
 #include "common.h"
 #include "params.h"
+#include "rope_norm.h"
 
 namespace h3 {
 
-
-struct Slot {
-    int a, b;       // chunk index (of 16) of the first-half chunk and its partner
-    int axis;       // 0 = t, 1 = h, 2 = w
-    int j0;         // frequency index of element 0 of chunk a inside its section
-    int width;      // section width s
-};
-
-__device__ __forceinline__ Slot slot_of(int p, int s0, int s1, int s2) {
-    const int w[3] = {s0, s1, s2};
-    int off = 0;
-    Slot r{0, 0, 0, 0, 16};
-#pragma unroll
-    for (int ax = 0; ax < 3; ++ax) {
-        const int cnt = w[ax] / 16;          // first-half chunks of this section
-        if (p >= 0 && p < cnt) {
-            r.a = off / 8 + p;
-            r.b = r.a + cnt;
-            r.axis = ax;
-            r.j0 = 8 * p;
-            r.width = w[ax];
-        }
-        p -= cnt;
-        off += w[ax];
-    }
-    return r;
-}
-
-__device__ __forceinline__ void unpack8(u32x4 v, float* f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16lo_to_f32(v[i]);
-        f[2 * i + 1] = bf16hi_to_f32(v[i]);
-    }
-}
-
-__device__ __forceinline__ float sum8lanes(float v) {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    return v;
-}
-
-// RMSNorm + rotation of one (token, head) pair of chunks; result rounded to bf16
-// and returned both as packed words and as the rounded fp32 values.
-__device__ __forceinline__ void norm_rotate(const float* xa, const float* xb, const float* ga,
-                                            const float* gb, const float* cs, const float* sn,
-                                            float eps, u32x4& oa, u32x4& ob, float* ra, float* rb) {
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss += xa[i] * xa[i] + xb[i] * xb[i];
-    ss = sum8lanes(ss);
-    const float rinv = rsqrtf(ss * (1.0f / kHeadDim) + eps);
-    float ya[8], yb[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float u = xa[i] * rinv * ga[i];
-        const float w = xb[i] * rinv * gb[i];
-        ya[i] = u * cs[i] - w * sn[i];
-        yb[i] = w * cs[i] + u * sn[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        oa[i] = pack_bf16x2(ya[2 * i], ya[2 * i + 1]);
-        ob[i] = pack_bf16x2(yb[2 * i], yb[2 * i + 1]);
-        ra[2 * i] = bf16lo_to_f32(oa[i]);
-        ra[2 * i + 1] = bf16hi_to_f32(oa[i]);
-        rb[2 * i] = bf16lo_to_f32(ob[i]);
-        rb[2 * i + 1] = bf16hi_to_f32(ob[i]);
-    }
-}
 
 __device__ __forceinline__ uint32_t quant4(const float* v, float inv) {
     uint32_t w = 0;
@@ -115,12 +45,13 @@ __device__ __forceinline__ uint32_t quant4(const float* v, float inv) {
 // sums of its bf16 values (into the K code buffer, used as scratch); after
 // ksum_reduce has turned them into the channel means, the last recomputes K'
 // alone and quantises fl32(k - mean).
-enum PrepMode { kPrepBf16 = 0, kPrepI8 = 1, kPrepI8Sums = 2, kPrepI8Smooth = 3 };
+// kPrepBf16K writes K' alone (for the forward that computes Q' in its prologue).
+enum PrepMode { kPrepBf16 = 0, kPrepI8 = 1, kPrepI8Sums = 2, kPrepI8Smooth = 3, kPrepBf16K = 4 };
 
 template <int kMode>
 __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
-    constexpr bool kInt8 = kMode != kPrepBf16;
-    constexpr bool kDoQ = kMode != kPrepI8Smooth;     // Q' produced in this pass
+    constexpr bool kInt8 = kMode == kPrepI8 || kMode == kPrepI8Sums || kMode == kPrepI8Smooth;
+    constexpr bool kDoQ = kMode != kPrepI8Smooth && kMode != kPrepBf16K;   // Q' produced in this pass
     constexpr bool kQuantK = kMode == kPrepI8 || kMode == kPrepI8Smooth;
     const int tid = threadIdx.x;
     const int row = tid >> 3;            // 0..31
@@ -131,21 +62,14 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
     int tok[2];
     bool valid[2];
     float cs[2][8], sn[2][8];
+    double freq[8];
+    rope_freqs(sl, P.rho0, P.rho1, P.rho2, freq);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         tok[t] = t0 + row + 32 * t;
         valid[t] = tok[t] < P.n;
-        // the angle pos * theta^(-2j/s) is formed and reduced in fp64: with positions
-        // in the thousands an fp32 product alone is off by ~1e-4 rad
         const double pv = valid[t] ? (double)P.pos[(int64_t)tok[t] * 3 + sl.axis] : 0.0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const double j = (double)(sl.j0 + i);
-            const double phi = pv * pow((double)P.theta, -2.0 * j / (double)sl.width);
-            const double two_pi = 6.283185307179586476925;
-            const float r = (float)(phi - two_pi * rint(phi / two_pi));
-            sincosf(r, &sn[t][i], &cs[t][i]);
-        }
+        rope_angles(pv, freq, cs[t], sn[t]);
     }
 
     float gqa[8], gqb[8], gka[8], gkb[8];
@@ -212,8 +136,10 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int64_t r = (head_base + tok[t]) * kHeadDim;
-                st16(qo + r + 8 * sl.a, oqa[t]);
-                st16(qo + r + 8 * sl.b, oqb[t]);
+                if constexpr (kDoQ) {
+                    st16(qo + r + 8 * sl.a, oqa[t]);
+                    st16(qo + r + 8 * sl.b, oqb[t]);
+                }
                 st16(ko + r + 8 * sl.a, oka[t]);
                 st16(ko + r + 8 * sl.b, okb[t]);
             }
@@ -331,6 +257,12 @@ hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream) {
         hipLaunchKernelGGL(prep_kernel<kPrepI8>, grid, block, 0, stream, P);
     else
         hipLaunchKernelGGL(prep_kernel<kPrepBf16>, grid, block, 0, stream, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_k(const PrepParams& P, hipStream_t stream) {
+    (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
+    hipLaunchKernelGGL(prep_kernel<kPrepBf16K>, dim3(P.npad / 64), dim3(256), 0, stream, P);
     return hipGetLastError();
 }
 

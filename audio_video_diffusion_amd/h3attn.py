@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG, "libh3attn.so")
 
 QK_BF16 = 0
 QK_I8_BLK64 = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_UNSUPPORTED", -4: "E_ALIGN",
           -5: "E_ALIAS", -6: "E_HIP"}
@@ -94,6 +94,9 @@ def _load():
         "h3attn_forward_fp8v": (ctypes.c_int, [pp, vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, vp]),
         "h3attn_debug_scores_i32": (ctypes.c_int, [pp, vp, vp, i32, i32, i32, i32, i32, vp, vp]),
         "h3attn_calibrate_mfma_bf16": (ctypes.c_int, [i32, i32, vp, vp]),
+        "h3attn_prep_k": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, vp, vp, vp]),
+        "h3attn_forward_fused_q": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, vp, vp, vp, i64, i64, vp, i64, i64,
+                                                  f32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -203,6 +206,31 @@ def forward(p: Problem, q_prep, k_prep, v, o, softmax_scale: float, q_scales=Non
                              _stream(stream))
     if rc:
         raise H3AttnError(rc, "h3attn_forward")
+
+
+def _gamma_stride(g):
+    return g.stride(0) if g.dim() == 2 else 0
+
+
+def prep_k(p: Problem, k, gamma_k, pos, k_out, stream=None):
+    """``h3attn_prep_k``: bf16 K' alone (k bf16 [N,H,d] view, gamma [d] or [H,d], pos int32 [N,3])."""
+    kp, kst, ksh = _nhd(k, "k")
+    rc = _lib.h3attn_prep_k(ctypes.byref(p), kp, kst, ksh, _ptr(gamma_k), _gamma_stride(gamma_k), _ptr(pos),
+                            _ptr(k_out), _stream(stream))
+    if rc:
+        raise H3AttnError(rc, "h3attn_prep_k")
+
+
+def forward_fused_q(p: Problem, q, gamma_q, pos, k_prep, v, o, softmax_scale: float, stream=None):
+    """``h3attn_forward_fused_q``: the bf16 forward from raw Q (q, v, o bf16 [N,H,d] views)."""
+    qp, qst, qsh = _nhd(q, "q")
+    vp, vst, vsh = _nhd(v, "v")
+    op, ost, osh = _nhd(o, "o")
+    rc = _lib.h3attn_forward_fused_q(ctypes.byref(p), qp, qst, qsh, _ptr(gamma_q), _gamma_stride(gamma_q),
+                                     _ptr(pos), _ptr(k_prep), vp, vst, vsh, op, ost, osh, float(softmax_scale),
+                                     _stream(stream))
+    if rc:
+        raise H3AttnError(rc, "h3attn_forward_fused_q")
 
 
 def alloc_v_fp8(p: Problem, device="cuda"):

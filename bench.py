@@ -160,12 +160,15 @@ def mfma_sustained(A, launches=6, blocks=2048, iters=6000):
     return statistics.median(rates[2:])
 
 
-def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=None, vfp8=None, kmean=None):
+def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=None, vfp8=None, kmean=None,
+              fused_q=False):
     """HIP-event times (ms) of prep and forward over `steps` calls after `warmup`.
 
     With ``vfp8 = (codes, scales)`` each step also stages V as E4M3 (timed on
     its own) and runs the FP8 P V forward; the third list holds those times.
     With ``kmean`` (fp32 [H, 128]) the int8 prep applies K smoothing.
+    With ``fused_q`` (bf16) the prep writes K' alone and the forward prepares
+    Q in its prologue (h3attn_prep_k + h3attn_forward_fused_q).
     """
     import torch
     q, k, v = dev["q"], dev["k"], dev["v"]
@@ -176,7 +179,9 @@ def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=No
     for i in range(warmup + steps):
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record()
-        if kmean is None:
+        if fused_q:
+            A.prep_k(p, k, dev["gamma_k"], dev["pos"], k_out)
+        elif kmean is None:
             A.prep(p, q, k, dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
         else:
             A.prep_ksmooth(p, q, k, dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks, kmean)
@@ -184,7 +189,9 @@ def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=No
         if vfp8 is not None:
             A.prep_v_fp8(p, v, vfp8[0], vfp8[1])
         e2.record()
-        if vfp8 is None:
+        if fused_q:
+            A.forward_fused_q(p, q, dev["gamma_q"], dev["pos"], k_out, v, o, scale)
+        elif vfp8 is None:
             A.forward(p, q_out, k_out, v, o, scale, qs, ks)
         else:
             A.forward_fp8v(p, q_out, k_out, vfp8[0], vfp8[1], o, scale, qs, ks)
@@ -200,24 +207,26 @@ def sweep(A, W, headline_dev, steps=3, warmup=1):
     """Forward throughput of every other workload: the remaining configurations,
     the headline's per-GPU head shards, the pages' block-24 shape, and the FP8
     P V variants (V staged as E4M3) on the headline, the 243-frame int8
-    workload and the block-24 shape.  The int8 Q/K + FP8 P V rows are the whole
-    quantised path of the pages, K smoothing included in their prep."""
+    workload and the block-24 shape, and the headline with Q prep fused into
+    the forward.  The int8 Q/K + FP8 P V rows are the whole quantised path of
+    the pages, K smoothing included in their prep."""
     import statistics
     import torch
     scale = 1.0 / math.sqrt(128.0)
     rows = []
-    # (seed, workload, head share of the headline tensors, Q/K int8, FP8 P V)
+    # (seed, workload, head share of the headline tensors, Q/K int8, FP8 P V, Q prep fused)
     hl = W.WORKLOADS[W.HEADLINE]
-    jobs = [(i, W.WORKLOADS[i], None, W.WORKLOADS[i].qk_int8, False)
+    jobs = [(i, W.WORKLOADS[i], None, W.WORKLOADS[i].qk_int8, False, False)
             for i in range(len(W.WORKLOADS)) if i != W.HEADLINE]
-    jobs += [(4, W.WORKLOADS[4], None, True, True)]
-    jobs += [(W.HEADLINE, w, w.heads, False, False) for w in W.SHARDS]
-    jobs += [(W.HEADLINE, hl, hl.heads, False, True), (W.HEADLINE, hl, hl.heads, True, True)]
-    jobs += [(100, W.BLOCK24, None, False, False), (100, W.BLOCK24, None, True, True)]
+    jobs += [(4, W.WORKLOADS[4], None, True, True, False)]
+    jobs += [(W.HEADLINE, w, w.heads, False, False, False) for w in W.SHARDS]
+    jobs += [(W.HEADLINE, hl, hl.heads, False, True, False), (W.HEADLINE, hl, hl.heads, True, True, False)]
+    jobs += [(W.HEADLINE, hl, hl.heads, False, False, True)]
+    jobs += [(100, W.BLOCK24, None, False, False, False), (100, W.BLOCK24, None, True, True, False)]
     cache = {}
-    for cfg, wl, shard_heads, int8, fp8v in jobs:
+    for cfg, wl, shard_heads, int8, fp8v, fused in jobs:
         print(f"[bench] sweep {wl.name}: N={wl.n_tokens} H={wl.heads} qk={'int8' if int8 else 'bf16'} "
-              f"pv={'fp8' if fp8v else 'bf16'}", file=sys.stderr, flush=True)
+              f"pv={'fp8' if fp8v else 'bf16'}{' q-prep fused' if fused else ''}", file=sys.stderr, flush=True)
         if shard_heads is not None:
             dev = headline_dev
         else:
@@ -234,14 +243,16 @@ def sweep(A, W, headline_dev, steps=3, warmup=1):
         kmean = torch.empty((wl.heads, 128), dtype=torch.float32, device="cuda") if ksm else None
         o = torch.empty((wl.n_tokens, wl.heads, 128), dtype=torch.bfloat16, device="cuda")
         prep_ms, fwd_ms, prepv_ms = time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup,
-                                              shard_heads, vfp8, kmean)
+                                              shard_heads, vfp8, kmean, fused)
         med = statistics.median(fwd_ms)
         tf = wl.flops / (med * 1e-3) / 1e12
         row = {"workload": wl.name, "n_tokens": wl.n_tokens, "heads": wl.heads,
                "qk": "int8" if int8 else "bf16", "pv": "fp8" if fp8v else "bf16", "k_smoothing": ksm,
+               "q_prep": "fused into the forward" if fused else "separate",
                "steps": steps,
                "forward_ms": {"median": round(med, 4), "min": round(min(fwd_ms), 4), "max": round(max(fwd_ms), 4)},
                "prep_ms": round(statistics.median(prep_ms), 4),
+               "step_ms": round(statistics.median([a + b + c for a, b, c in zip(prep_ms, fwd_ms, prepv_ms)]), 4),
                "forward_tflops": round(tf, 2), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
         if fp8v:
             row["prep_v_ms"] = round(statistics.median(prepv_ms), 4)

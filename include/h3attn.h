@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 4
+#define H3ATTN_ABI_VERSION 5
 
 typedef enum {
     H3ATTN_OK = 0,
@@ -252,6 +252,44 @@ int h3attn_forward_fp8v(const h3attn_problem* p,
                         const void* v_codes, const float* v_scales,
                         void* o, int64_t o_stride_tok, int64_t o_stride_head,
                         float softmax_scale, void* stream);
+
+/*
+ * h3attn_prep_k - the K half of h3attn_prep in the bf16 format: writes K'
+ * (bf16 [H][N_pad][128], rows n >= N zero) exactly as h3attn_prep does, and
+ * no Q'.  It supplies h3attn_forward_fused_q, which prepares Q itself.
+ * k, gamma_k, pos_thw, k_out: as for h3attn_prep; k_out must not overlap an
+ * input.  Requires qk_format == H3ATTN_QK_BF16 (E_UNSUPPORTED otherwise).
+ * Errors: as for h3attn_prep.
+ */
+int h3attn_prep_k(const h3attn_problem* p,
+                  const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                  const void* gamma_k, int64_t gamma_head_stride,
+                  const int32_t* pos_thw, void* k_out, void* stream);
+
+/*
+ * h3attn_forward_fused_q - h3attn_forward in the bf16 format with the Q half
+ * of h3attn_prep moved into the forward: each work-group computes the Q' rows
+ * it owns from raw Q (RMSNorm + 3-axis RoPE as in h3attn_prep, the same
+ * arithmetic and the same bits) while its first K'/V tiles load, so Q' is
+ * never written to or read from memory.  This removes the prep -> forward
+ * boundary for Q, the entry-fusion step of the quantised path ("H3 Runtime
+ * Current State", Owned Performance Kernels: the fused entry kernel that the
+ * pages measured and the direct-layout boundary-removal target).  The output
+ * is bit-identical to h3attn_prep followed by h3attn_forward.
+ * q, gamma_q, pos_thw: as for h3attn_prep (raw Q view, its RMSNorm weight,
+ *            the (t, h, w) positions).
+ * k_prep:    bf16 K' from h3attn_prep_k (or h3attn_prep) for the same descriptor.
+ * v, o, softmax_scale: as for h3attn_forward; o must not overlap any input.
+ * Requires qk_format == H3ATTN_QK_BF16 (E_UNSUPPORTED otherwise).
+ * Errors: as for h3attn_prep.
+ */
+int h3attn_forward_fused_q(const h3attn_problem* p,
+                           const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                           const void* gamma_q, int64_t gamma_head_stride, const int32_t* pos_thw,
+                           const void* k_prep,
+                           const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                           void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                           float softmax_scale, void* stream);
 
 /*
  * h3attn_debug_scores_i32 - test hook for the int8 format: the exact int32

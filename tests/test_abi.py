@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 4
+    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 5
     for s in (0, -1, -2, -3, -4, -5, -6, 7):
         assert A.lib.h3attn_status_string(s)
 
@@ -239,3 +239,49 @@ def test_binding_rejects_non_nhd_views():
     x = torch.zeros(4, 1, 128, dtype=torch.bfloat16).transpose(1, 2)
     with pytest.raises(ValueError):
         A.forward(p, x, x, x, x, 0.1)
+
+
+def prep_k(p, k=G, kst=384, ksh=128, gk=H, gsh=0, pos=I, ko=J):
+    return A.lib.h3attn_prep_k(ctypes.byref(p), k, kst, ksh, gk, gsh, pos, ko, None)
+
+
+def fwd_fq(p, q=F, qst=384, qsh=128, gq=H, gsh=0, pos=I, k=G, v=K, vst=384, vsh=128, o=J, ost=384, osh=128,
+           scale=0.088):
+    return A.lib.h3attn_forward_fused_q(ctypes.byref(p), q, qst, qsh, gq, gsh, pos, k, v, vst, vsh, o, ost, osh,
+                                        scale, None)
+
+
+def test_prep_k_checks():
+    p = A.problem(1000, 3)
+    assert prep_k(A.problem(1000, 3, A.QK_I8_BLK64)) == -3   # K' alone only in bf16
+    assert prep_k(A.problem(1000, 3, head_dim=64)) == -3
+    assert prep_k(p, k=None) == -1
+    assert prep_k(p, gk=None) == -1
+    assert prep_k(p, pos=None) == -1
+    assert prep_k(p, ko=None) == -1
+    assert prep_k(p, k=G + 2) == -4
+    assert prep_k(p, kst=383) == -4
+    assert prep_k(p, gsh=4) == -4
+    assert prep_k(p, ko=J + 8) == -4
+    assert prep_k(p, ko=G + 384 * 10) == -5                 # output on top of k
+    assert prep_k(p, ko=I - 64) == -5                       # overlaps positions
+    assert prep_k(p, ko=H - 64) == -5                       # overlaps gamma
+
+
+def test_forward_fused_q_checks():
+    p = A.problem(1000, 3)
+    assert fwd_fq(A.problem(1000, 3, A.QK_I8_BLK64)) == -3  # bf16 only
+    for kw in ("q", "gq", "pos", "k", "v", "o"):
+        assert fwd_fq(p, **{kw: None}) == -1, kw
+    assert fwd_fq(p, q=F + 2) == -4
+    assert fwd_fq(p, qst=100) == -4
+    assert fwd_fq(p, gsh=4) == -4
+    assert fwd_fq(p, pos=I + 2) == -4
+    assert fwd_fq(p, k=G + 8) == -4
+    assert fwd_fq(p, scale=0.0) == -2
+    assert fwd_fq(p, ost=128, osh=128) == -2                 # output rows overlap each other
+    assert fwd_fq(p, o=F + 384 * 10) == -5                   # output over raw q
+    assert fwd_fq(p, o=H - 64) == -5                         # output over gamma_q
+    assert fwd_fq(p, o=I + 64) == -5                         # output over the positions
+    assert fwd_fq(p, o=G + 4096) == -5                       # output inside k'
+    assert fwd_fq(p, o=K + 384 * 10) == -5                   # output inside v
