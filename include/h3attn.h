@@ -107,7 +107,10 @@ size_t h3attn_v_scales_bytes(const h3attn_problem* p);
  *                            y[o+j+s/2] cos phi + y[o+j] sin phi)
  * ("H3 Runtime Current State", Owned Performance Kernels: Q/K RMSNorm and
  * split-half RoPE; "H3 Blackwell Runtime Plan", Architecture: 3-axis RoPE).
- * Arithmetic is fp32; the result is rounded once to bf16.
+ * Arithmetic is fp32; the result is rounded once to bf16.  phi is formed and
+ * reduced in fp64 (theta^(-2j/s) as the j-th power of theta^(-2/s), reduction
+ * by multiples of pi/2) and cos/sin are evaluated in fp32 from their Taylor
+ * series on |r| <= pi/4: absolute error about 1e-7.
  *
  * bf16 format: q_out/k_out are bf16 [H][N_pad][128] (HND, row stride 128).
  * int8 format: the bf16-rounded values of each head are grouped in blocks of
