@@ -39,9 +39,9 @@ PEAK_HBM_GBS = 8000.0
 # csrc/forward.hip no longer hashes to `source_sha256`, traffic is null.
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
-    "source_sha256": "e2622cd31e61e9d17a6543c35d07fc0552a9126872b14979ff83b3da4323acc7",
-    "fetch_kib": 13332855.8, "fetch_scale": 2.0,
-    "write_kib": 809104.5, "write_scale": 1.0,
+    "source_sha256": "cf97b99b5c29fe6ec7843497da9ee78f703f85f55e80e228f591cba937da3cbf",
+    "fetch_kib": 13332857.6, "fetch_scale": 2.0,
+    "write_kib": 813012.3, "write_scale": 1.0,
 }
 
 
