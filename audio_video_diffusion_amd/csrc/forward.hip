@@ -145,9 +145,12 @@ __device__ __forceinline__ void mfma_s(f32x16& d, const bf16x8& a, const bf16x8&
 
 // The int8 form of mfma_s: int32 scores in arch VGPRs (the softmax converts
 // them there), Q' codes in AGPRs.
-__device__ __forceinline__ void mfma_s_i8(i32x16& d, const i32x4& a, const i32x4& b, bool first) {
+// The chain's first product adds to c0 (the int8 forward passes the bits of
+// 1.5 * 2^23 in every element; see kI8Bias).
+__device__ __forceinline__ void mfma_s_i8(i32x16& d, const i32x4& a, const i32x4& b, bool first,
+                                          const i32x16& c0) {
     if (first)
-        asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+        asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c0));
     else
         asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
@@ -302,6 +305,17 @@ struct DmaOffsets8 {
     }
 };
 
+// Int8 scores: |S| <= 127 * 127 * 128 < 2^22, so an int32 accumulator that
+// starts at the bit pattern of 1.5 * 2^23 ends holding the fp32 value
+// 1.5 * 2^23 + S exactly (the magic-number conversion), and no per-score
+// int -> float conversion is needed.  The bias is taken out of the row max
+// exactly (a subtraction of nearby values) and out of each logit together
+// with the running max, in the FMA that applies the scale: one constant per
+// tile, fl(1.5 * 2^23 * coef + m), whose rounding (at most 0.75 * coef, under
+// one unit of S) is common to every score of the row in that tile.
+constexpr float kI8Bias = 12582912.0f;             // 1.5 * 2^23
+constexpr int32_t kI8BiasBits = 0x4b400000;
+
 // log2 of the factor applied to P before it is rounded to E4M3: the lazily
 // rescaled P is at most 2^8, times 2^0.8 stays below 448, E4M3's largest
 // finite value, so more of P's range lands on normal E4M3 numbers.  The
@@ -379,6 +393,9 @@ fwd8_kernel(FwdParams P) {
         rope_freqs(fsl, P.rho0, P.rho1, P.rho2, ffreq);
     }
     float qscale = 1.f;
+    i32x16 bias16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bias16[e] = kI8BiasBits;
     if constexpr (kInt8) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
     // K block scales through the constant address space: one scalar load per
     // tile, counted by lgkmcnt.  A vector load would be waited for with
@@ -446,16 +463,16 @@ fwd8_kernel(FwdParams P) {
             i32x16 Si[2];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                mfma_s_i8(Si[0], a[0][t], q[t], t == 0);
-                mfma_s_i8(Si[1], a[1][t], q[t], t == 0);
+                mfma_s_i8(Si[0], a[0][t], q[t], t == 0, bias16);
+                mfma_s_i8(Si[1], a[1][t], q[t], t == 0, bias16);
             }
             // wait states before the VALU reads the matrix core's results
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(Si[0]), "+v"(Si[1]));
-            // |S| <= 127 * 127 * 128 < 2^24: exact in fp32
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) S[kb][e] = (float)Si[kb][e];
+            // the fp32 values 1.5 * 2^23 + S (kI8Bias).  Whole-vector bit casts: a
+            // bit cast of a single vector element is miscompiled by this compiler
+            // (every such read returns element 0).
+            S[0] = __builtin_bit_cast(f32x16, Si[0]);
+            S[1] = __builtin_bit_cast(f32x16, Si[1]);
         } else {
             bf16x8 a[2][8];
 #pragma unroll
@@ -491,7 +508,7 @@ fwd8_kernel(FwdParams P) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kb][e]);
-        mx = max_halves(mx) * coef;
+        mx = kInt8 ? (max_halves(mx) - kI8Bias) * coef : max_halves(mx) * coef;
         if (__any(mx > m + kRescaleLog2)) {
             const float mm = fmaxf(m, mx);
             const float alpha = __builtin_amdgcn_exp2f(m - mm);
@@ -503,7 +520,9 @@ fwd8_kernel(FwdParams P) {
         if constexpr (kFp8V) {
             // P' = 2^0.8 * P rounded to E4M3, 32 consecutive keys per lane half;
             // the row sum adds the fp32 P' before rounding
-            const float mb = m - kPLog2Fp8;
+            const float mb0 = m - kPLog2Fp8;
+            // int8: the score bias leaves with the max (kI8Bias)
+            const float mb = kInt8 ? __builtin_fmaf(kI8Bias, coef, mb0) : mb0;
             i32x8 Pf;
             float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -537,6 +556,8 @@ fwd8_kernel(FwdParams P) {
             }
         } else {
             bf16x8 Pb[2][2];
+            // int8: the score bias leaves with the max (kI8Bias)
+            const float mk = kInt8 ? __builtin_fmaf(kI8Bias, coef, m) : m;
             float rs[2] = {0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -546,8 +567,8 @@ fwd8_kernel(FwdParams P) {
 #pragma unroll
                     for (int ii = 0; ii < 4; ++ii) {
                         const int e = 8 * s + 2 * ii;
-                        float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -m));
-                        float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], coef, -m));
+                        float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mk));
+                        float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], coef, -mk));
                         if (masked) {
                             if (j * kBN + key_of_elem(kb, e, hh) >= n) x0 = 0.f;
                             if (j * kBN + key_of_elem(kb, e + 1, hh) >= n) x1 = 0.f;
