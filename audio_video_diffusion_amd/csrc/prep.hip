@@ -74,8 +74,10 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
 
     float gqa[8], gqb[8], gka[8], gkb[8];
     auto load_gamma = [&](int h) {
-        unpack8(ld16(P.gq + h * P.g_sh + 8 * sl.a), gqa);
-        unpack8(ld16(P.gq + h * P.g_sh + 8 * sl.b), gqb);
+        if constexpr (kDoQ) {            // gamma_q is absent (NULL) when Q' is not produced
+            unpack8(ld16(P.gq + h * P.g_sh + 8 * sl.a), gqa);
+            unpack8(ld16(P.gq + h * P.g_sh + 8 * sl.b), gqb);
+        }
         unpack8(ld16(P.gk + h * P.g_sh + 8 * sl.a), gka);
         unpack8(ld16(P.gk + h * P.g_sh + 8 * sl.b), gkb);
     };
