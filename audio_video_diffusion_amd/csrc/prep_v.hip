@@ -16,9 +16,10 @@
 // plain 128-bit LDS loads.
 //
 // Four launches on one stream: clear the 128 x H absmax words (a fill kernel,
-// not a memset), absmax over tokens (atomic max of the non-negative fp32 bit
-// patterns: order-independent, so the result is deterministic), quantise and
-// transpose, then turn each absmax into its scale in place.
+// not a memset), absmax over tokens (partial maxima per 512-token block, then
+// an atomic max of the non-negative fp32 bit patterns: order-independent, so
+// the result is deterministic), quantise and transpose, then turn each absmax
+// into its scale in place.
 #include "common.h"
 #include "params.h"
 
@@ -29,20 +30,47 @@ __global__ void __launch_bounds__(256) vfp8_clear(uint32_t* amax, int count) {
     if (i < count) amax[i] = 0u;
 }
 
-// One work-group per 64-token block: thread (head-chunk, channel) scans the
-// block's tokens.  Grid (npad / 64, ceil(H * 128 / 256)).
+// Channel absmax: one work-group per (512-token block, 64 groups of 8
+// channels).  Thread (g, q) = (tid % 64, tid / 64) reads 16 bytes (8 channels)
+// of every 4th token of the block, so a wave covers 1 KB of one token row per
+// load; the four token phases meet in LDS and one atomic max per channel
+// leaves the work-group.  Grid (ceil(N / 512), ceil(H * 16 / 64)).
+constexpr int kAbsTokens = 512;
+
 __global__ void __launch_bounds__(256) vfp8_absmax(PrepVParams P) {
-    const int hc = blockIdx.y * 256 + threadIdx.x;       // head * 128 + channel
-    if (hc >= P.h * 128) return;
-    const int head = hc >> 7, ch = hc & 127;
-    const int t0 = blockIdx.x * 64;
-    const int t1 = min(t0 + 64, P.n);
-    float a = 0.f;
-    for (int t = t0; t < t1; ++t) {
-        const uint16_t b = P.v[(int64_t)t * P.v_st + (int64_t)head * P.v_sh + ch];
-        a = fmaxf(a, fabsf(__uint_as_float((uint32_t)b << 16)));
+    __shared__ float part[4][64][9];                 // [token phase][group][channel], padded
+    const int g = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int c8 = blockIdx.y * 64 + g;              // head * 16 + channel group
+    const bool live = c8 < P.h * 16;
+    const int head = c8 >> 4, ch0 = (c8 & 15) * 8;
+    const int t0 = blockIdx.x * kAbsTokens;
+    const int t1 = min(t0 + kAbsTokens, P.n);
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = 0.f;
+    if (live) {
+        const uint16_t* base = P.v + (int64_t)head * P.v_sh + ch0;
+#pragma unroll 8
+        for (int t = t0 + q; t < t1; t += 4) {
+            const u32x4 w = ld16(base + (int64_t)t * P.v_st);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                a[2 * k] = fmaxf(a[2 * k], fabsf(bf16lo_to_f32(w[k])));
+                a[2 * k + 1] = fmaxf(a[2 * k + 1], fabsf(bf16hi_to_f32(w[k])));
+            }
+        }
     }
-    if (a > 0.f) atomicMax(reinterpret_cast<unsigned int*>(P.scales) + hc, __float_as_uint(a));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[q][g][i] = a[i];
+    __syncthreads();
+    if (q == 0 && live) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float m = fmaxf(fmaxf(part[0][g][i], part[1][g][i]), fmaxf(part[2][g][i], part[3][g][i]));
+            if (m > 0.f)
+                atomicMax(reinterpret_cast<unsigned int*>(P.scales) + head * 128 + ch0 + i, __float_as_uint(m));
+        }
+    }
 }
 
 // One work-group per (64-token tile, head): 64 tokens x 128 channels.
@@ -100,7 +128,8 @@ hipError_t launch_prep_v(const PrepVParams& P, hipStream_t stream) {
     const int count = P.h * 128;
     const int cb = (count + 255) / 256;
     hipLaunchKernelGGL(vfp8_clear, dim3(cb), dim3(256), 0, stream, reinterpret_cast<uint32_t*>(P.scales), count);
-    hipLaunchKernelGGL(vfp8_absmax, dim3(P.npad / 64, cb), dim3(256), 0, stream, P);
+    hipLaunchKernelGGL(vfp8_absmax, dim3((P.n + kAbsTokens - 1) / kAbsTokens, (P.h * 16 + 63) / 64), dim3(256), 0,
+                       stream, P);
     hipLaunchKernelGGL(vfp8_quant, dim3(P.npad / 64, P.h), dim3(256), 0, stream, P);
     hipLaunchKernelGGL(vfp8_finalize, dim3(cb), dim3(256), 0, stream, P.scales, count);
     return hipGetLastError();
