@@ -74,33 +74,36 @@ __global__ void __launch_bounds__(256) vfp8_absmax(PrepVParams P) {
 }
 
 // One work-group per (64-token tile, head): 64 tokens x 128 channels.
-// Thread t handles channel pair 2*(t & 63) (+1) for 16 tokens (t >> 6) + 4i;
-// codes go through LDS to leave d-major.
+// Thread t handles the 8 channels 8 * (t & 15) of the tokens (t >> 4) + 16i,
+// i < 4, with 16-byte loads (a wave reads four 256-byte token rows); codes go
+// through LDS to leave d-major.
 __global__ void __launch_bounds__(256) vfp8_quant(PrepVParams P) {
     __shared__ __attribute__((aligned(16))) uint8_t tile[128][64 + 4];                 // [d][key], padded rows
     const int tid = threadIdx.x;
     const int head = blockIdx.y;
     const int t0 = blockIdx.x * 64;
-    const int cp = tid & 63, tq = tid >> 6;
-    const int c0 = 2 * cp;
-    const float* amax = P.scales + (int64_t)head * 128;
-    const float a0 = amax[c0], a1 = amax[c0 + 1];
-    const float inv0 = a0 > 0.f ? 448.0f / a0 : 0.f;
-    const float inv1 = a1 > 0.f ? 448.0f / a1 : 0.f;
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-        const int key = tq + 4 * i;
+    const int c0 = 8 * (tid & 15), tq = tid >> 4;
+    const float* amax = P.scales + (int64_t)head * 128 + c0;
+    float inv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float a = amax[i];
+        inv[i] = a > 0.f ? 448.0f / a : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int key = tq + 16 * i;
         const int tok = t0 + key;
-        uint32_t w = 0;
-        if (tok < P.n) {
-            const uint32_t two =
-                *reinterpret_cast<const uint32_t*>(P.v + (int64_t)tok * P.v_st + (int64_t)head * P.v_sh + c0);
-            const float x0 = fminf(fmaxf(__uint_as_float(two << 16) * inv0, -448.f), 448.f);
-            const float x1 = fminf(fmaxf(__uint_as_float(two & 0xffff0000u) * inv1, -448.f), 448.f);
-            w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (tok < P.n) w = ld16(P.v + (int64_t)tok * P.v_st + (int64_t)head * P.v_sh + c0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float x0 = fminf(fmaxf(bf16lo_to_f32(w[k]) * inv[2 * k], -448.f), 448.f);
+            const float x1 = fminf(fmaxf(bf16hi_to_f32(w[k]) * inv[2 * k + 1], -448.f), 448.f);
+            const uint32_t b = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+            tile[c0 + 2 * k][key] = (uint8_t)(b & 0xff);
+            tile[c0 + 2 * k + 1][key] = (uint8_t)((b >> 8) & 0xff);
         }
-        tile[c0][key] = (uint8_t)(w & 0xff);
-        tile[c0 + 1][key] = (uint8_t)((w >> 8) & 0xff);
     }
     __syncthreads();
     // 8 KB out: thread t writes 32 bytes = half a d-row
