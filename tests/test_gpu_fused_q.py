@@ -134,3 +134,29 @@ def test_fused_full_workload_bitwise_and_sampled_rows():
     for hh in (0, wl.heads - 1):
         check(got[:, hh, :], oracle_rows_bf16(inp, hh, rows), what=f"fused {wl.name} head {hh}")
     assert np.isfinite(got).all()
+
+
+def test_fused_output_into_head_major_view():
+    wl = W.ragged_workload(1500, 3)
+    dev = W.device_inputs(W.make_inputs(414, wl))
+    n, h = wl.n_tokens, wl.heads
+    p = problem_for(wl)
+    q_out, k_full, _, _ = run_prep(p, dev)
+    plain = run_forward(p, q_out, k_full, dev["v"])
+    hnd = torch.full((h, n, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    run_fused(p, dev, run_prep_k(p, dev), o=hnd.permute(1, 0, 2))
+    assert same_bits(hnd.permute(1, 0, 2).contiguous(), plain)
+
+
+def test_fused_block24_shape_bitwise():
+    # the pages' block-24 attention shape: 37,810 tokens, 56 heads
+    wl = W.BLOCK24
+    print(f"    {wl.name} N={wl.n_tokens} H={wl.heads}", flush=True)
+    dev = W.device_inputs(W.make_inputs(100, wl))
+    p = problem_for(wl)
+    q_out, k_full, _, _ = run_prep(p, dev)
+    plain = run_forward(p, q_out, k_full, dev["v"])
+    del q_out
+    k_only = run_prep_k(p, dev)
+    assert same_bits(k_only, k_full)
+    assert same_bits(run_fused(p, dev, k_only), plain)
