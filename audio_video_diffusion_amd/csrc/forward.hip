@@ -12,7 +12,9 @@
 //   owns one 32-row block and keeps its Q' rows in registers.  Waves w and
 //   w+4 share a SIMD: per wave the state is small (O^T in 64 AGPRs), so two
 //   waves fit each SIMD's register file and the hardware overlaps one wave's
-//   softmax with the other's matrix-core work;
+//   softmax with the other's matrix-core work.  With int8 K' and E4M3 V the
+//   work-group has four waves and 128 rows instead, and two of them share a
+//   CU (see kW);
 // * the work-group streams K'/V in tiles of 64 keys through four LDS stages,
 //   fetched three tiles ahead with buffer -> LDS DMA (buffer_load_dwordx4 ...
 //   lds: 1 KB per wave instruction, no registers in between; each wave moves
@@ -271,27 +273,31 @@ __global__ void __launch_bounds__(256) scores_i8_kernel(ScoreParams P) {
 // ============================================================================
 // The forward kernel (see the file comment).
 // ============================================================================
-template <bool kInt8, bool kFp8V>
+template <bool kInt8, bool kFp8V, int kW>
 struct DmaOffsets8 {
     static constexpr int kRowB = kInt8 ? 128 : 256;   // K' row bytes
-    static constexpr int kN = kInt8 ? 1 : 2;          // K' DMA instructions per wave
-    static constexpr int kNV = kFp8V ? 1 : 2;         // V DMA instructions per wave
+    static constexpr int kRowsPW = 64 / kW;           // K' rows moved per wave
+    static constexpr int kN = kRowsPW * kRowB / 1024; // K' DMA instructions per wave
+    static constexpr int kNV = kFp8V ? (128 / kW) * 64 / 1024 : 2;   // V DMA instructions per wave
     uint32_t k[kN], v[kNV], vlast[kNV];
     __device__ __forceinline__ DmaOffsets8(int wave, int lane, int64_t v_st, int last_key0, int n) {
-        // each wave moves K' rows 8w..8w+7: 8 (int8) or 4 (bf16) rows per instruction
+        // wave w moves K' rows kRowsPW * w ...: 8 (int8) or 4 (bf16) rows per instruction
         constexpr int cpr = kRowB / 16, rpi = 64 / cpr;
 #pragma unroll
         for (int r = 0; r < kN; ++r) {
-            const int rho = 8 * wave + rpi * r + lane / cpr;
+            const int rho = kRowsPW * wave + rpi * r + lane / cpr;
             const int c = (lane % cpr) ^ (rho & (cpr - 1));
             k[r] = (uint32_t)((kFp8V ? key_of_row_f8(rho) : key_of_row(rho)) * kRowB + c * 16);
         }
         if constexpr (kFp8V) {
-            // E4M3 V^T tile [128 d][64 keys]: wave w moves d-rows 16w..16w+15;
-            // LDS slot s of row d holds 16-byte chunk s ^ ((d >> 2) & 3)
-            const int d = 16 * wave + (lane >> 2);
-            const int c = (lane & 3) ^ ((d >> 2) & 3);
-            v[0] = vlast[0] = (uint32_t)(d * 64 + c * 16);
+            // E4M3 V^T tile [128 d][64 keys]: wave w moves d-rows (128 / kW) w ...,
+            // 16 per instruction; LDS slot s of row d holds 16-byte chunk s ^ ((d >> 2) & 3)
+#pragma unroll
+            for (int r = 0; r < kNV; ++r) {
+                const int d = (128 / kW) * wave + 16 * r + (lane >> 2);
+                const int c = (lane & 3) ^ ((d >> 2) & 3);
+                v[r] = vlast[r] = (uint32_t)(d * 64 + c * 16);
+            }
         } else {
             const uint32_t rs = (uint32_t)(v_st * 2);
 #pragma unroll
@@ -325,11 +331,19 @@ constexpr float kPLog2Fp8 = 0.8f;
 // kFuseQ (bf16 only): Q' is not read from memory but computed in the prologue
 // from raw Q with the prep kernel's own per-row routine (rope_norm.h), so the
 // result is bit-identical to prep + forward.
-template <bool kInt8, bool kFp8V, bool kFuseQ = false>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// kW = 4 (int8 K' with E4M3 V only): four waves own 128 query rows and the
+// stages take 64 KB of LDS, so two independent work-groups share each CU (one
+// wave of each per SIMD).  Their barriers are unrelated, so the two waves of a
+// SIMD drift out of phase and one's softmax covers the other's matrix-core
+// phases, also at the tile edges where the eight-wave form keeps them in step;
+// each row's arithmetic is unchanged.
+template <bool kInt8, bool kFp8V, bool kFuseQ = false, int kW = 8>
+__global__ void __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd8_kernel(FwdParams P) {
     static_assert(!(kFuseQ && kInt8), "the fused Q prologue produces bf16 Q'");
-    using D = DmaOffsets8<kInt8, kFp8V>;
+    static_assert(kW == 8 || (kW == 4 && kInt8 && kFp8V), "four waves: int8 K' with E4M3 V only");
+    constexpr int kBMw = 32 * kW;                  // query rows per work-group
+    using D = DmaOffsets8<kInt8, kFp8V, kW>;
     constexpr int kKTileB = kBN * D::kRowB;        // 16 KB (bf16) or 8 KB (int8)
     constexpr int kVTileB = kBN * (kFp8V ? 128 : 256);   // 8 KB (E4M3) or 16 KB (bf16)
     constexpr int kDma8 = D::kN + D::kNV;          // DMA instructions per wave per tile
@@ -348,7 +362,7 @@ fwd8_kernel(FwdParams P) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n32 = lane & 31, hh = lane >> 5;
-    const int q0 = qt * kBM + wave * 32;
+    const int q0 = qt * kBMw + wave * 32;
     const int n = P.n;
 
     const uint8_t* qhead = static_cast<const uint8_t*>(P.q) + (int64_t)head * P.npad * D::kRowB;
@@ -425,11 +439,12 @@ fwd8_kernel(FwdParams P) {
         const u32x4 kr = raw_rsrc(khead + (int64_t)kt * kKTileB);
 #pragma unroll
         for (int r = 0; r < D::kN; ++r)
-            dma16_buf(kr, dmo.k[r], kbuf(t) + (8 * wave + (kInt8 ? 8 : 4) * r) * D::kRowB);
+            dma16_buf(kr, dmo.k[r], kbuf(t) + (D::kRowsPW * wave + (kInt8 ? 8 : 4) * r) * D::kRowB);
         if constexpr (kFp8V) {
             // pad keys of the last tile are zero codes in memory: no clamp
             const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kVTileB);
-            dma16_buf(vr, dmo.v[0], vbuf(t) + 1024 * wave);
+#pragma unroll
+            for (int r = 0; r < D::kNV; ++r) dma16_buf(vr, dmo.v[r], vbuf(t) + 1024 * (D::kNV * wave + r));
         } else {
             const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kBN * P.v_st * 2);
             const bool lt = kt == last;
@@ -683,8 +698,8 @@ fwd8_kernel(FwdParams P) {
 hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
     const dim3 grid(kXcds * P.per_xcd), block(512);
-    if (int8 && fp8v)
-        hipLaunchKernelGGL((fwd8_kernel<true, true>), grid, block, 0, stream, P);
+    if (int8 && fp8v)      // four waves, 128-row tiles (forward_tile_rows), plain block order
+        hipLaunchKernelGGL((fwd8_kernel<true, true, false, 4>), dim3(P.total), dim3(256), 0, stream, P);
     else if (int8)
         hipLaunchKernelGGL((fwd8_kernel<true, false>), grid, block, 0, stream, P);
     else if (fp8v)
@@ -699,6 +714,8 @@ hipError_t launch_forward_fused_q(const FwdParams& P, hipStream_t stream) {
     hipLaunchKernelGGL((fwd8_kernel<false, false, true>), dim3(kXcds * P.per_xcd), dim3(512), 0, stream, P);
     return hipGetLastError();
 }
+
+int forward_tile_rows(bool int8, bool fp8v) { return int8 && fp8v ? 128 : kBM; }
 
 hipError_t launch_scores_i8(const ScoreParams& P, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call

@@ -43,7 +43,7 @@ struct FwdParams {
     int sec0, sec1, sec2;
     uint16_t* o; int64_t o_st, o_sh;
     int n, h, npad, nblk;
-    int qtiles;             // ceil(N / 256)
+    int qtiles;             // ceil(N / forward_tile_rows(...))
     int total;              // H * qtiles
     int per_xcd;            // ceil(total / 8)
     float c;                // softmax_scale * log2(e)
@@ -61,6 +61,8 @@ hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream);
 hipError_t launch_prep_k(const PrepParams& P, hipStream_t stream);
 hipError_t launch_prep_ksmooth(const PrepParams& P, hipStream_t stream);
 hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t stream);
+// query rows per work-group of that forward (FwdParams::qtiles counts tiles of this size)
+int forward_tile_rows(bool int8, bool fp8v);
 // bf16 Q'/K', V through its view, Q' computed from raw Q in the prologue
 hipError_t launch_forward_fused_q(const FwdParams& P, hipStream_t stream);
 hipError_t launch_prep_v(const PrepVParams& P, hipStream_t stream);
