@@ -39,9 +39,9 @@ PEAK_HBM_GBS = 8000.0
 # csrc/forward.hip no longer hashes to `source_sha256`, traffic is null.
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
-    "source_sha256": "4a2b409c9c5f24a1e15d9acc97f1f36712a5e5a50a826a8363f06b3a7fe3fd31",
-    "fetch_kib": 13332853.9, "fetch_scale": 2.0,
-    "write_kib": 811810.9, "write_scale": 1.0,
+    "source_sha256": "1e1b54b061aa07dfd9d32ba3f83ef2680df86db00ab7c29f9391e043bd4e3d91",
+    "fetch_kib": 13332851.9, "fetch_scale": 2.0,
+    "write_kib": 806041.1, "write_scale": 1.0,
 }
 
 
