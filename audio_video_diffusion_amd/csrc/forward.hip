@@ -552,7 +552,10 @@ fwd8_kernel(FwdParams P) {
                         if (masked && j * kBN + key_of<true>(kb, e, hh) >= n) x[u] = 0.f;
                         rs[u] += x[u];
                     }
-                    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                    // the first conversion fills the low half and keeps the high half of
+                    // its third operand, which the second overwrites: any live value
+                    // serves there (a constant 0 would cost a register move per word)
+                    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __float_as_int(x[0]), false);
                     wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wd, true);
                     Pf[4 * kb + w4] = wd;
                 }
