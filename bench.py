@@ -39,9 +39,9 @@ PEAK_HBM_GBS = 8000.0
 # csrc/forward.hip no longer hashes to `source_sha256`, traffic is null.
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
-    "source_sha256": "1e1b54b061aa07dfd9d32ba3f83ef2680df86db00ab7c29f9391e043bd4e3d91",
+    "source_sha256": "b316cfbca4efbc3e10cc12b5b5cc73e2fa24dbf77cf7736e4f0f3254fd296c83",
     "fetch_kib": 13332851.9, "fetch_scale": 2.0,
-    "write_kib": 806041.1, "write_scale": 1.0,
+    "write_kib": 811990.2, "write_scale": 1.0,
 }
 
 
