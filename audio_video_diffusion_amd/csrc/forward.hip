@@ -58,6 +58,12 @@ constexpr int kBM = 256;            // query rows per work-group
 constexpr int kBN = 64;             // keys per tile
 constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;
+// A lane's tile row sum (32 keys) at most this bounds each of its P by it, so
+// every logit is at most 7 = log2(128) above the running max: no raise needed.
+constexpr float kSumCheck = 128.0f;
+// The same for the FP8 P.V form, whose P' carries the factor 2^0.8:
+// 200 < 2^(7 + 0.8) = 222.9.
+constexpr float kSumCheckFp8 = 200.0f;
 
 // LDS tile sizes in bytes; four stages of each are in flight
 constexpr int kStages = 4;          // LDS stages of the K'/V stream
@@ -518,48 +524,73 @@ fwd8_kernel(FwdParams P) {
                 for (int e = 0; e < 16; ++e)
                     if (j * kBN + key_of<kFp8V>(kb, e, hh) >= n) S[kb][e] = -FLT_MAX;
         }
-        float mx = S[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kb][e]);
-        mx = kInt8 ? (max_halves(mx) - kI8Bias) * coef : max_halves(mx) * coef;
-        if (__any(mx > m + kRescaleLog2)) {
-            const float mm = fmaxf(m, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m - mm);
-            m = mm;
-            l *= alpha;
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) scale_acc(O[cc], alpha);
-        }
-        if constexpr (kFp8V) {
-            // P' = 2^0.8 * P rounded to E4M3, 32 consecutive keys per lane half;
-            // the row sum adds the fp32 P' before rounding
-            const float mb0 = m - kPLog2Fp8;
-            // int8: the score bias leaves with the max (kI8Bias)
-            const float mb = kInt8 ? __builtin_fmaf(kI8Bias, coef, mb0) : mb0;
-            i32x8 Pf;
-            float rs[4] = {0.f, 0.f, 0.f, 0.f};
+        // P is formed from the running max m as it stands.  The row max of the
+        // tile is only needed when m may have to be raised: a lane whose 32
+        // probabilities sum to at most kSumCheck has every P <= kSumCheck, i.e.
+        // every base-2 logit at most log2(kSumCheck) = 7 above m, one unit short
+        // of the rescale threshold.  So the max is computed, and the raise
+        // decided exactly as before, only for the (rare) tiles where some lane's
+        // sum exceeds that bound, and for the ragged last tile; P is recomputed
+        // only if m was raised.  The rescale decisions, hence the results, are
+        // those of computing the max for every tile.
+        auto raise_max = [&]() -> bool {
+            float mx = S[0][0];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int w4 = 0; w4 < 4; ++w4) {
-                    float x[4];
+                for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kb][e]);
+            mx = kInt8 ? (max_halves(mx) - kI8Bias) * coef : max_halves(mx) * coef;
+            if (__any(mx > m + kRescaleLog2)) {
+                const float mm = fmaxf(m, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m - mm);
+                m = mm;
+                l *= alpha;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int e = 4 * w4 + u;
-                        x[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mb));
-                        if (masked && j * kBN + key_of<true>(kb, e, hh) >= n) x[u] = 0.f;
-                        rs[u] += x[u];
+                for (int cc = 0; cc < 4; ++cc) scale_acc(O[cc], alpha);
+                return true;
+            }
+            return false;
+        };
+        if constexpr (kFp8V) {
+            // P' = 2^0.8 * P rounded to E4M3, 32 consecutive keys per lane half;
+            // the row sum adds the fp32 P' before rounding
+            i32x8 Pf;
+            float rs[4];
+            auto make_p = [&]() {
+                const float mb0 = m - kPLog2Fp8;
+                // int8: the score bias leaves with the max (kI8Bias)
+                const float mb = kInt8 ? __builtin_fmaf(kI8Bias, coef, mb0) : mb0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) rs[u] = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int w4 = 0; w4 < 4; ++w4) {
+                        float x[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int e = 4 * w4 + u;
+                            x[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mb));
+                            if (masked && j * kBN + key_of<true>(kb, e, hh) >= n) x[u] = 0.f;
+                            rs[u] += x[u];
+                        }
+                        // the first conversion fills the low half and keeps the high half of
+                        // its third operand, which the second overwrites: any live value
+                        // serves there (a constant 0 would cost a register move per word)
+                        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __float_as_int(x[0]), false);
+                        wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wd, true);
+                        Pf[4 * kb + w4] = wd;
                     }
-                    // the first conversion fills the low half and keeps the high half of
-                    // its third operand, which the second overwrites: any live value
-                    // serves there (a constant 0 would cost a register move per word)
-                    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __float_as_int(x[0]), false);
-                    wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wd, true);
-                    Pf[4 * kb + w4] = wd;
+            };
+            make_p();
+            float t = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+            // P' carries the factor 2^0.8: 2^7.64 = 200 < 2^(7 + 0.8)
+            if (masked || __any(!(t <= kSumCheckFp8)))
+                if (raise_max()) {
+                    make_p();
+                    t = (rs[0] + rs[1]) + (rs[2] + rs[3]);
                 }
-            l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+            l += t;
             // O^T += V^T P'^T: lane (n32, hh) reads d-row 32cc + n32, keys 32hh..32hh+31
             const uint8_t* vb_ = vbuf(j) + v_lane_off;
             const int s0 = ((2 * hh) ^ v_sw) * 16, s1 = ((2 * hh + 1) ^ v_sw) * 16;
@@ -574,31 +605,41 @@ fwd8_kernel(FwdParams P) {
             }
         } else {
             bf16x8 Pb[2][2];
-            // int8: the score bias leaves with the max (kI8Bias)
-            const float mk = kInt8 ? __builtin_fmaf(kI8Bias, coef, m) : m;
-            float rs[2] = {0.f, 0.f};
+            float rs[2];
+            auto make_p = [&]() {
+                // int8: the score bias leaves with the max (kI8Bias)
+                const float mk = kInt8 ? __builtin_fmaf(kI8Bias, coef, m) : m;
+                rs[0] = rs[1] = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    u32x4 w;
+                    for (int s = 0; s < 2; ++s) {
+                        u32x4 w;
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        const int e = 8 * s + 2 * ii;
-                        float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mk));
-                        float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], coef, -mk));
-                        if (masked) {
-                            if (j * kBN + key_of_elem(kb, e, hh) >= n) x0 = 0.f;
-                            if (j * kBN + key_of_elem(kb, e + 1, hh) >= n) x1 = 0.f;
+                        for (int ii = 0; ii < 4; ++ii) {
+                            const int e = 8 * s + 2 * ii;
+                            float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mk));
+                            float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], coef, -mk));
+                            if (masked) {
+                                if (j * kBN + key_of_elem(kb, e, hh) >= n) x0 = 0.f;
+                                if (j * kBN + key_of_elem(kb, e + 1, hh) >= n) x1 = 0.f;
+                            }
+                            const f32x2 f = {x0, x1};
+                            const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+                            rs[s] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs[s], false);
+                            w[ii] = __builtin_bit_cast(uint32_t, b);
                         }
-                        const f32x2 f = {x0, x1};
-                        const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
-                        rs[s] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs[s], false);
-                        w[ii] = __builtin_bit_cast(uint32_t, b);
+                        Pb[kb][s] = __builtin_bit_cast(bf16x8, w);
                     }
-                    Pb[kb][s] = __builtin_bit_cast(bf16x8, w);
+            };
+            make_p();
+            float t = rs[0] + rs[1];
+            if (masked || __any(!(t <= kSumCheck)))
+                if (raise_max()) {
+                    make_p();
+                    t = rs[0] + rs[1];
                 }
-            l += rs[0] + rs[1];
+            l += t;
             // O^T += V^T P^T
             const uint8_t* vb_ = vbuf(j);
             typedef short i16x4 __attribute__((ext_vector_type(4)));
