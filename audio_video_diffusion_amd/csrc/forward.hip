@@ -151,6 +151,12 @@ __device__ __forceinline__ void mfma_s(f32x16& d, const bf16x8& a, const bf16x8&
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
+// The chain's first product of the fused-Q form: it adds to c0, which holds
+// -m in every element (the running max leaves with the start value).
+__device__ __forceinline__ void mfma_s_from(f32x16& d, const bf16x8& a, const bf16x8& b, const f32x16& c0) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c0));
+}
+
 // The int8 form of mfma_s: int32 scores in arch VGPRs (the softmax converts
 // them there), Q' codes in AGPRs.
 // The chain's first product adds to c0 (the int8 forward passes the bits of
@@ -335,8 +341,9 @@ constexpr int32_t kI8BiasBits = 0x4b400000;
 constexpr float kPLog2Fp8 = 0.8f;
 
 // kFuseQ (bf16 only): Q' is not read from memory but computed in the prologue
-// from raw Q with the prep kernel's own per-row routine (rope_norm.h), so the
-// result is bit-identical to prep + forward.
+// from raw Q with the prep kernel's own per-row routine (rope_norm.h), rounded
+// to bf16 once with the base-2 logit factor folded in; each Q'K'^T chain then
+// starts from -m, so the scores leave the matrix core ready for exp2.
 // kW = 4 (int8 K' with E4M3 V only): four waves own 128 query rows and the
 // stages take 64 KB of LDS, so two independent work-groups share each CU (one
 // wave of each per SIMD).  Their barriers are unrelated, so the two waves of a
@@ -433,6 +440,11 @@ fwd8_kernel(FwdParams P) {
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) O[cc] = f32x16{};
     float m = -INFINITY, l = 0.f;
+    // kFuseQ: Q' carries the base-2 logit scale, and every Q'K'^T chain starts
+    // from -mch (negm), so the scores come out as logit - mch, ready for exp2.
+    // mch is the running max except before the first tile (m = -inf, mch = 0).
+    float mch = 0.f;
+    f32x16 negm = f32x16{};
 
     const int ntiles = (n + kBN - 1) / kBN;
     const int last = ntiles - 1;
@@ -505,8 +517,13 @@ fwd8_kernel(FwdParams P) {
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                mfma_s(S[0], a[0][t], q[t], t == 0);
-                mfma_s(S[1], a[1][t], q[t], t == 0);
+                if (kFuseQ && t == 0) {
+                    mfma_s_from(S[0], a[0][t], q[t], negm);
+                    mfma_s_from(S[1], a[1][t], q[t], negm);
+                } else {
+                    mfma_s(S[0], a[0][t], q[t], t == 0);
+                    mfma_s(S[1], a[1][t], q[t], t == 0);
+                }
             }
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]), "+v"(S[1]));
         }
@@ -539,7 +556,7 @@ fwd8_kernel(FwdParams P) {
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kb][e]);
-            mx = kInt8 ? (max_halves(mx) - kI8Bias) * coef : max_halves(mx) * coef;
+            mx = kInt8 ? (max_halves(mx) - kI8Bias) * coef : kFuseQ ? max_halves(mx) + mch : max_halves(mx) * coef;
             if (__any(mx > m + kRescaleLog2)) {
                 const float mm = fmaxf(m, mx);
                 const float alpha = __builtin_amdgcn_exp2f(m - mm);
@@ -606,9 +623,12 @@ fwd8_kernel(FwdParams P) {
         } else {
             bf16x8 Pb[2][2];
             float rs[2];
-            auto make_p = [&]() {
+            // shifted (kFuseQ, after m was raised): the scores still hold
+            // logit - mch, so m - mch more is subtracted
+            auto make_p = [&](const bool shifted) {
                 // int8: the score bias leaves with the max (kI8Bias)
                 const float mk = kInt8 ? __builtin_fmaf(kI8Bias, coef, m) : m;
+                const float off = mch - m;
                 rs[0] = rs[1] = 0.f;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
@@ -618,8 +638,14 @@ fwd8_kernel(FwdParams P) {
 #pragma unroll
                         for (int ii = 0; ii < 4; ++ii) {
                             const int e = 8 * s + 2 * ii;
-                            float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mk));
-                            float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], coef, -mk));
+                            float x0, x1;
+                            if constexpr (kFuseQ) {
+                                x0 = __builtin_amdgcn_exp2f(shifted ? S[kb][e] + off : S[kb][e]);
+                                x1 = __builtin_amdgcn_exp2f(shifted ? S[kb][e + 1] + off : S[kb][e + 1]);
+                            } else {
+                                x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mk));
+                                x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], coef, -mk));
+                            }
                             if (masked) {
                                 if (j * kBN + key_of_elem(kb, e, hh) >= n) x0 = 0.f;
                                 if (j * kBN + key_of_elem(kb, e + 1, hh) >= n) x1 = 0.f;
@@ -632,12 +658,18 @@ fwd8_kernel(FwdParams P) {
                         Pb[kb][s] = __builtin_bit_cast(bf16x8, w);
                     }
             };
-            make_p();
+            make_p(false);
             float t = rs[0] + rs[1];
-            if (masked || __any(!(t <= kSumCheck)))
+            // kFuseQ: the first tile sets the running max (its chain started from 0)
+            if (masked || (kFuseQ && j == 0) || __any(!(t <= kSumCheck)))
                 if (raise_max()) {
-                    make_p();
+                    make_p(true);
                     t = rs[0] + rs[1];
+                    if constexpr (kFuseQ) {
+                        mch = m;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) negm[e] = -m;
+                    }
                 }
             l += t;
             // O^T += V^T P^T
@@ -689,7 +721,8 @@ fwd8_kernel(FwdParams P) {
                 unpack8(fqa[ps], xa);
                 unpack8(fqb[ps], xb);
                 u32x4 oa, ob;
-                norm_rotate(xa, xb, ga, gb, cs, sn, P.eps, oa, ob, ra, rb);
+                // Q' is rounded to bf16 once, with the base-2 logit scale folded in
+                norm_rotate<true>(xa, xb, ga, gb, cs, sn, P.eps, oa, ob, ra, rb, P.c);
                 if (qt * kBM + 64 * ps + r >= n) oa = ob = u32x4{0, 0, 0, 0};
                 uint8_t* st = (s == 0 ? kbuf(3) : vbuf(3)) + r * 256;
                 *reinterpret_cast<u32x4*>(st + ((fsl.a ^ (r & 15)) * 16)) = oa;

@@ -65,10 +65,14 @@ __device__ __forceinline__ float sum8lanes(float v) {
 // RMSNorm + rotation of one (token, head) pair of chunks; result rounded to bf16
 // and returned both as packed words and as the rounded fp32 values.  Every
 // rounding is spelled out (no contraction), so the prep kernel and the
-// forward's prologue produce the same bits from the same inputs.
+// forward's prologue produce the same bits from the same inputs.  With
+// kPostScale the fp32 result is multiplied by `post` before the one bf16
+// rounding (the forward's fused prologue folds the logit scale in there).
+template <bool kPostScale = false>
 __device__ __forceinline__ void norm_rotate(const float* xa, const float* xb, const float* ga,
                                             const float* gb, const float* cs, const float* sn,
-                                            float eps, u32x4& oa, u32x4& ob, float* ra, float* rb) {
+                                            float eps, u32x4& oa, u32x4& ob, float* ra, float* rb,
+                                            float post = 1.0f) {
 #pragma clang fp contract(off)
     float ss = 0.f;
 #pragma unroll
@@ -85,6 +89,10 @@ __device__ __forceinline__ void norm_rotate(const float* xa, const float* xb, co
         const float w = (xb[i] * rinv) * gb[i];
         ya[i] = __builtin_fmaf(u, cs[i], -(w * sn[i]));
         yb[i] = __builtin_fmaf(w, cs[i], u * sn[i]);
+        if constexpr (kPostScale) {
+            ya[i] = ya[i] * post;
+            yb[i] = yb[i] * post;
+        }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

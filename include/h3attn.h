@@ -272,13 +272,17 @@ int h3attn_prep_k(const h3attn_problem* p,
 /*
  * h3attn_forward_fused_q - h3attn_forward in the bf16 format with the Q half
  * of h3attn_prep moved into the forward: each work-group computes the Q' rows
- * it owns from raw Q (RMSNorm + 3-axis RoPE as in h3attn_prep, the same
- * arithmetic and the same bits) while its first K'/V tiles load, so Q' is
- * never written to or read from memory.  This removes the prep -> forward
- * boundary for Q, the entry-fusion step of the quantised path ("H3 Runtime
- * Current State", Owned Performance Kernels: the fused entry kernel that the
- * pages measured and the direct-layout boundary-removal target).  The output
- * is bit-identical to h3attn_prep followed by h3attn_forward.
+ * it owns from raw Q (RMSNorm + 3-axis RoPE with the arithmetic of
+ * h3attn_prep) while its first K'/V tiles load, so Q' is never written to or
+ * read from memory.  This removes the prep -> forward boundary for Q, the
+ * entry-fusion step of the quantised path ("H3 Runtime Current State", Owned
+ * Performance Kernels: the fused entry kernel that the pages measured and the
+ * direct-layout boundary-removal target).  Since Q' stays inside the kernel,
+ * it is rounded to bf16 once with the base-2 logit factor
+ * softmax_scale * log2(e) already applied (one rounding, as for h3attn_prep's
+ * Q'), and the running row max enters as the start value of each Q'K'^T
+ * product; the output therefore agrees with h3attn_prep + h3attn_forward to
+ * within bf16 rounding of Q', not bit for bit.
  * q, gamma_q, pos_thw: as for h3attn_prep (raw Q view, its RMSNorm weight,
  *            the (t, h, w) positions).
  * k_prep:    bf16 K' from h3attn_prep_k (or h3attn_prep) for the same descriptor.

@@ -1,11 +1,12 @@
 """GPU tests of the Q-prep fusion: h3attn_prep_k + h3attn_forward_fused_q.
 
-The fused forward computes Q' in its prologue with the prep kernel's own
-per-row routine, so its output must equal h3attn_prep + h3attn_forward bit for
-bit, and the K-only prep must equal the K' of the full prep bit for bit (pad
-rows included).  The plain path is checked against the oracle in the parity
-tests; the tiny workload and the 129,410-token workload are also checked
-against the oracle here.
+The fused forward computes Q' in its prologue with the prep kernel's per-row
+routine, but rounds it to bf16 once with the base-2 logit scale folded in
+(bf16(scale * log2(e) * Q') instead of bf16(Q')), so its output is checked
+against the CPU oracle rather than bit for bit against h3attn_prep +
+h3attn_forward.  The K-only prep must equal the K' of the full prep bit for
+bit (pad rows included), and the fused forward's own output must not depend on
+the input/output strides or on the call.
 """
 import numpy as np
 import pytest
@@ -45,63 +46,97 @@ def same_bits(a, b):
     return torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def oracle_full(inp, sections=W.ROPE_SECTIONS, theta=W.ROPE_THETA, eps=W.RMS_EPS):
+    qp = O.prep(inp.q, inp.gamma_q, inp.pos, sections, theta, eps)
+    kp = O.prep(inp.k, inp.gamma_k, inp.pos, sections, theta, eps)
+    return O.attention(qp, kp, O.bf16_bits_to_f64(inp.v), SCALE)
+
+
 @pytest.mark.parametrize("n,h,per_head,seed", [
     (1, 1, False, 401), (2, 2, True, 402), (63, 1, False, 403), (64, 2, False, 404), (255, 1, True, 405),
     (256, 3, False, 406), (257, 2, True, 407), (511, 1, False, 408), (1000, 3, True, 409), (4099, 2, False, 410),
 ])
-def test_fused_matches_prep_then_forward_bitwise(n, h, per_head, seed):
+def test_fused_matches_oracle(n, h, per_head, seed):
     wl = W.ragged_workload(n, h)
     print(f"    N={n} H={h} per_head_gamma={per_head}", flush=True)
-    dev = W.device_inputs(W.make_inputs(seed, wl, per_head_gamma=per_head))
+    inp = W.make_inputs(seed, wl, per_head_gamma=per_head)
+    dev = W.device_inputs(inp)
     p = problem_for(wl)
-    q_out, k_full, _, _ = run_prep(p, dev)
+    _, k_full, _, _ = run_prep(p, dev)
     k_only = run_prep_k(p, dev)
     assert same_bits(k_only, k_full)
-    plain = run_forward(p, q_out, k_full, dev["v"])
-    fused = run_fused(p, dev, k_only)
-    assert same_bits(fused, plain)
+    got = f64(run_fused(p, dev, k_only))
+    ref = oracle_full(inp)
+    if n == 1:
+        # one key: softmax weight exactly 1, so O is V exactly
+        assert np.array_equal(got, O.bf16_bits_to_f64(inp.v))
+    check(got, ref, what=f"fused N={n}")
+
+
+def test_fused_sharp_softmax_no_less_accurate_than_prep_then_forward():
+    # gamma x 4: logits ~16x sharper, the running max is raised many times
+    # along the row (rescale path with the max carried in the chain start).
+    # At such logits the bf16 rounding of Q'/K' alone moves the output by
+    # more than the N(0,1) bounds, for either path; the fused path's error
+    # against the exact result must stay within that of prep + forward.
+    from gpu_util import errors
+    wl = W.ragged_workload(3001, 2)
+    inp = W.make_inputs(415, wl)
+    four = O.f32_to_bf16_bits((O.bf16_bits_to_f64(inp.gamma_q) * 4).astype(np.float32))
+    inp.gamma_q = four
+    inp.gamma_k = four
+    dev = W.device_inputs(inp)
+    p = problem_for(wl)
+    ref = oracle_full(inp)
+    q_out, k_full, _, _ = run_prep(p, dev)
+    e_plain = errors(f64(run_forward(p, q_out, k_full, dev["v"])), ref)
+    got = f64(run_fused(p, dev, run_prep_k(p, dev)))
+    e_fused = errors(got, ref)
+    print(f"    max/mean/rel_l2: fused {e_fused}, prep + forward {e_plain}", flush=True)
+    assert np.isfinite(got).all()
+    for ef, ep in zip(e_fused, e_plain):
+        assert ef <= 1.5 * ep + 1e-3, (e_fused, e_plain)
 
 
 @pytest.mark.parametrize("sections,theta,eps", [((64, 32, 32), 500.0, 1e-5), ((16, 16, 96), 1e6, 0.0)])
 def test_fused_other_rope_sections_and_constants(sections, theta, eps):
     wl = W.ragged_workload(1500, 2)
-    dev = W.device_inputs(W.make_inputs(411, wl, per_head_gamma=True))
+    inp = W.make_inputs(411, wl, per_head_gamma=True)
+    dev = W.device_inputs(inp)
     p = A.problem(wl.n_tokens, wl.heads, sections=sections, theta=theta, eps=eps)
-    q_out, k_full, _, _ = run_prep(p, dev)
+    _, k_full, _, _ = run_prep(p, dev)
     k_only = run_prep_k(p, dev)
     assert same_bits(k_only, k_full)
-    assert same_bits(run_fused(p, dev, k_only), run_forward(p, q_out, k_full, dev["v"]))
+    check(f64(run_fused(p, dev, k_only)), oracle_full(inp, sections, theta, eps),
+          what=f"fused sections={sections}")
 
 
 def test_fused_tiny_workload_against_oracle():
-    wl = W.WORKLOADS[0]
     inp = W.make_inputs(0)
     dev = W.device_inputs(inp)
-    p = problem_for(wl)
-    o = run_fused(p, dev, run_prep_k(p, dev))
-    qp = O.prep(inp.q, inp.gamma_q, inp.pos, W.ROPE_SECTIONS, W.ROPE_THETA, W.RMS_EPS)
-    kp = O.prep(inp.k, inp.gamma_k, inp.pos, W.ROPE_SECTIONS, W.ROPE_THETA, W.RMS_EPS)
-    check(f64(o), O.attention(qp, kp, O.bf16_bits_to_f64(inp.v), SCALE), what="fused tiny")
+    p = problem_for(W.WORKLOADS[0])
+    check(f64(run_fused(p, dev, run_prep_k(p, dev))), oracle_full(inp), what="fused tiny")
 
 
 def test_fused_on_interleaved_views_and_strided_output():
     # raw Q, K, V as views of one interleaved projection output [N, 3, H, d];
-    # O into every other 128-wide slot of [N, H, 2, d]
+    # O into every other 128-wide slot of [N, H, 2, d]: the same bits as the
+    # contiguous call
     wl = W.ragged_workload(777, 3)
     inp = W.make_inputs(412, wl, per_head_gamma=True)
     n, h = wl.n_tokens, wl.heads
+    dev = W.device_inputs(inp)
+    p = problem_for(wl)
+    plain = run_fused(p, dev, run_prep_k(p, dev))
     qkv = torch.empty((n, 3, h, 128), dtype=torch.bfloat16, device="cuda")
     for i, bits in enumerate((inp.q, inp.k, inp.v)):
         qkv[:, i] = W.bits_to_torch(bits)
-    dev = W.device_inputs(inp)
     dev["q"], dev["k"], dev["v"] = qkv[:, 0], qkv[:, 1], qkv[:, 2]
-    p = problem_for(wl)
-    q_out, k_full, _, _ = run_prep(p, dev)
-    plain = run_forward(p, q_out, k_full, dev["v"])
     obuf = torch.full((n, h, 2, 128), 7.0, dtype=torch.bfloat16, device="cuda")
     run_fused(p, dev, run_prep_k(p, dev), o=obuf[:, :, 0])
     assert torch.all(obuf[:, :, 1] == 7.0)
     assert same_bits(obuf[:, :, 0].contiguous(), plain)
+    check(f64(plain), oracle_full(inp), what="fused interleaved")
 
 
 def test_fused_repeated_calls_are_deterministic():
@@ -114,7 +149,7 @@ def test_fused_repeated_calls_are_deterministic():
         assert same_bits(run_fused(p, dev, k_only), first)
 
 
-def test_fused_full_workload_bitwise_and_sampled_rows():
+def test_fused_full_workload_sampled_rows():
     cfg = W.HEADLINE
     wl = W.WORKLOADS[cfg]
     print(f"    {wl.name} N={wl.n_tokens} H={wl.heads}", flush=True)
@@ -128,12 +163,14 @@ def test_fused_full_workload_bitwise_and_sampled_rows():
     assert same_bits(k_only, k_full)
     del k_full
     fused = run_fused(p, dev, k_only)
-    assert same_bits(fused, plain)
     rows = sample_rows(wl, n_random=32)
-    got = f64(fused[torch.from_numpy(rows).cuda()])
+    sel = torch.from_numpy(rows).cuda()
+    got, got_plain = f64(fused[sel]), f64(plain[sel])
     for hh in (0, wl.heads - 1):
-        check(got[:, hh, :], oracle_rows_bf16(inp, hh, rows), what=f"fused {wl.name} head {hh}")
-    assert np.isfinite(got).all()
+        ref = oracle_rows_bf16(inp, hh, rows)
+        check(got[:, hh, :], ref, what=f"fused {wl.name} head {hh}")
+        check(got_plain[:, hh, :], ref, what=f"prep + forward {wl.name} head {hh}")
+    assert torch.isfinite(fused.float()).all()
 
 
 def test_fused_output_into_head_major_view():
@@ -141,22 +178,26 @@ def test_fused_output_into_head_major_view():
     dev = W.device_inputs(W.make_inputs(414, wl))
     n, h = wl.n_tokens, wl.heads
     p = problem_for(wl)
-    q_out, k_full, _, _ = run_prep(p, dev)
-    plain = run_forward(p, q_out, k_full, dev["v"])
+    k_only = run_prep_k(p, dev)
+    tok = run_fused(p, dev, k_only)
     hnd = torch.full((h, n, 128), 3.0, dtype=torch.bfloat16, device="cuda")
-    run_fused(p, dev, run_prep_k(p, dev), o=hnd.permute(1, 0, 2))
-    assert same_bits(hnd.permute(1, 0, 2).contiguous(), plain)
+    run_fused(p, dev, k_only, o=hnd.permute(1, 0, 2))
+    assert same_bits(hnd.permute(1, 0, 2).contiguous(), tok)
 
 
-def test_fused_block24_shape_bitwise():
+def test_fused_block24_shape_sampled_rows():
     # the pages' block-24 attention shape: 37,810 tokens, 56 heads
     wl = W.BLOCK24
     print(f"    {wl.name} N={wl.n_tokens} H={wl.heads}", flush=True)
-    dev = W.device_inputs(W.make_inputs(100, wl))
+    inp = W.make_inputs(100, wl)
+    dev = W.device_inputs(inp)
     p = problem_for(wl)
-    q_out, k_full, _, _ = run_prep(p, dev)
-    plain = run_forward(p, q_out, k_full, dev["v"])
-    del q_out
+    _, k_full, _, _ = run_prep(p, dev)
     k_only = run_prep_k(p, dev)
     assert same_bits(k_only, k_full)
-    assert same_bits(run_fused(p, dev, k_only), plain)
+    del k_full
+    fused = run_fused(p, dev, k_only)
+    rows = sample_rows(wl, n_random=32)
+    got = f64(fused[torch.from_numpy(rows).cuda()])
+    for hh in (0, wl.heads - 1):
+        check(got[:, hh, :], oracle_rows_bf16(inp, hh, rows), what=f"fused {wl.name} head {hh}")
