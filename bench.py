@@ -1,12 +1,16 @@
 #!/usr/bin/env python3
 """Throughput of the packed-attention hot path on one MI355X.
 
-One step = h3attn_prep (Q/K RMSNorm + 3-axis RoPE + head-major layout) then
-h3attn_forward (non-causal attention over the whole packed sequence) on one
-batch of seeded synthetic inputs already resident in HBM.
+One step = the whole hot path on one batch of seeded synthetic inputs already
+resident in HBM: Q/K RMSNorm + 3-axis RoPE + head-major layout, then non-causal
+attention over the whole packed sequence.  In the bf16 format the step is
+h3attn_prep_k (K') then h3attn_forward_fused_q (Q' prepared in the forward's
+prologue); with --q-prep separate, or with int8 Q/K or FP8 P V, it is
+h3attn_prep then h3attn_forward (or h3attn_forward_fp8v).
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
-                    [--qk bf16|int8] [--pv bf16|fp8] [--headline-only]
+                    [--qk bf16|int8] [--pv bf16|fp8] [--q-prep fused|separate]
+                    [--headline-only]
 
 Prints one JSON line.  ``value`` is attention TFLOP/s (4 N^2 d H per step)
 over the whole step; ``roofline`` rates the forward kernel alone against the
@@ -30,31 +34,41 @@ PEAK_INT8_TOPS = 5033.2
 PEAK_FP8_TFLOPS = 5033.2      # dense E4M3 matrix-core rate
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per h3attn_forward launch on the 1344x768/124-frame bf16 workload,
-# from two rocprofv3 --pmc passes over one bench step (FETCH_SIZE, then
-# WRITE_SIZE, KiB per dispatch).  Each is scaled by what the same counter
-# reports for a plain 1 GiB device copy (bench.py --copy-probe 1024): FETCH_SIZE
-# reads 524,309 KiB there (factor 2.0), WRITE_SIZE 1,048,576 KiB (factor 1.0).
-# The figure belongs to the kernel source it was taken on: when
-# csrc/forward.hip no longer hashes to `source_sha256`, traffic is null.
+# HBM bytes per launch of the forward kernel the bf16 step runs
+# (h3attn_forward_fused_q) on the 1344x768/124-frame workload, from two
+# rocprofv3 --pmc passes over one bench step (FETCH_SIZE, then WRITE_SIZE, KiB
+# per dispatch).  Each is scaled by what the same counter reports for a plain
+# 1 GiB device copy (bench.py --copy-probe 1024).  The figure belongs to the
+# kernel sources it was taken on: when csrc/forward.hip + csrc/rope_norm.h no
+# longer hash to `source_sha256`, traffic is null.
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
-    "source_sha256": "b316cfbca4efbc3e10cc12b5b5cc73e2fa24dbf77cf7736e4f0f3254fd296c83",
-    "fetch_kib": 13332851.9, "fetch_scale": 2.0,
-    "write_kib": 811990.2, "write_scale": 1.0,
+    "kernel": "h3attn_forward_fused_q",
+    "source_sha256": "8d5e23f582e04f447cf227bbe1ad0150431fc0094f253eaa0ca59b38d1984830",
+    # the copy's kernel reads 524,309 KiB per 1 GiB as FETCH_SIZE (factor 2.0) and
+    # writes 1,048,576 KiB as WRITE_SIZE (factor 1.0)
+    "fetch_kib": 13507449.6, "fetch_scale": 2.0,
+    "write_kib": 778098.2, "write_scale": 1.0,
 }
 
 
-def forward_traffic(workload_name):
-    """Counter-measured HBM bytes per forward launch, or None if stale/other workload."""
+def kernel_sources_sha256():
+    """sha256 over the forward kernel's sources (forward.hip, then rope_norm.h)."""
     import hashlib
+    h = hashlib.sha256()
+    for name in ("forward.hip", "rope_norm.h"):
+        with open(os.path.join(ROOT, "audio_video_diffusion_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def forward_traffic(workload_name, fused):
+    """Counter-measured HBM bytes per forward launch, or None if stale/other workload/kernel."""
     t = FORWARD_TRAFFIC
-    if workload_name != t["workload"]:
+    if workload_name != t["workload"] or not fused or t["source_sha256"] is None:
         return None
-    path = os.path.join(ROOT, "audio_video_diffusion_amd", "csrc", "forward.hip")
     try:
-        with open(path, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        digest = kernel_sources_sha256()
     except OSError:
         return None
     if digest != t["source_sha256"]:
@@ -77,6 +91,9 @@ def parse():
                     help="Q/K format of the timed step (default: the workload's own)")
     ap.add_argument("--pv", choices=("bf16", "fp8"), default="bf16",
                     help="P V product: bf16, or E4M3 V (staged each step) on the FP8 matrix cores")
+    ap.add_argument("--q-prep", choices=("fused", "separate"), default="fused",
+                    help="bf16 Q/K with bf16 P V: Q' prepared in the forward's prologue (default) "
+                         "or by h3attn_prep before h3attn_forward")
     ap.add_argument("--copy-probe", type=int, default=None, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration) and exit")
     return ap.parse_args()
@@ -207,8 +224,8 @@ def sweep(A, W, headline_dev, steps=3, warmup=1):
     """Forward throughput of every other workload: the remaining configurations,
     the headline's per-GPU head shards, the pages' block-24 shape, and the FP8
     P V variants (V staged as E4M3) on the headline, the 243-frame int8
-    workload and the block-24 shape, and the headline with Q prep fused into
-    the forward.  The int8 Q/K + FP8 P V rows are the whole quantised path of
+    workload and the block-24 shape, and the headline with the separate Q prep
+    (h3attn_prep + h3attn_forward).  The int8 Q/K + FP8 P V rows are the whole quantised path of
     the pages, K smoothing included in their prep."""
     import statistics
     import torch
@@ -216,13 +233,14 @@ def sweep(A, W, headline_dev, steps=3, warmup=1):
     rows = []
     # (seed, workload, head share of the headline tensors, Q/K int8, FP8 P V, Q prep fused)
     hl = W.WORKLOADS[W.HEADLINE]
-    jobs = [(i, W.WORKLOADS[i], None, W.WORKLOADS[i].qk_int8, False, False)
+    # bf16 Q/K with bf16 P V: Q prep fused into the forward, as in the timed step
+    jobs = [(i, W.WORKLOADS[i], None, W.WORKLOADS[i].qk_int8, False, not W.WORKLOADS[i].qk_int8)
             for i in range(len(W.WORKLOADS)) if i != W.HEADLINE]
     jobs += [(4, W.WORKLOADS[4], None, True, True, False)]
-    jobs += [(W.HEADLINE, w, w.heads, False, False, False) for w in W.SHARDS]
+    jobs += [(W.HEADLINE, w, w.heads, False, False, True) for w in W.SHARDS]
     jobs += [(W.HEADLINE, hl, hl.heads, False, True, False), (W.HEADLINE, hl, hl.heads, True, True, False)]
-    jobs += [(W.HEADLINE, hl, hl.heads, False, False, True)]
-    jobs += [(100, W.BLOCK24, None, False, False, False), (100, W.BLOCK24, None, True, True, False)]
+    jobs += [(W.HEADLINE, hl, hl.heads, False, False, False)]
+    jobs += [(100, W.BLOCK24, None, False, False, True), (100, W.BLOCK24, None, True, True, False)]
     cache = {}
     for cfg, wl, shard_heads, int8, fp8v, fused in jobs:
         print(f"[bench] sweep {wl.name}: N={wl.n_tokens} H={wl.heads} qk={'int8' if int8 else 'bf16'} "
@@ -288,6 +306,7 @@ def main():
     wl = W.WORKLOADS[cfg]
     int8 = wl.qk_int8 if args.qk is None else args.qk == "int8"
     fp8v = args.pv == "fp8"
+    fused = args.q_prep == "fused" and not (int8 or fp8v)
     print(f"[bench] generating {wl.name}: N={wl.n_tokens} H={wl.heads}", file=sys.stderr, flush=True)
     inp = W.make_inputs(cfg, threads=16)
     dev = W.device_inputs(inp)
@@ -304,12 +323,17 @@ def main():
         if timed is not None:
             e0, e1, e2 = ev(), ev(), ev()
             e0.record()
-        A.prep(p, dev["q"], dev["k"], dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
+        if fused:
+            A.prep_k(p, dev["k"], dev["gamma_k"], dev["pos"], k_out)
+        else:
+            A.prep(p, dev["q"], dev["k"], dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
         if fp8v:
             A.prep_v_fp8(p, dev["v"], v_codes, v_scales)
         if timed is not None:
             e1.record()
-        if fp8v:
+        if fused:
+            A.forward_fused_q(p, dev["q"], dev["gamma_q"], dev["pos"], k_out, dev["v"], o, scale)
+        elif fp8v:
             A.forward_fp8v(p, q_out, k_out, v_codes, v_scales, o, scale, qs, ks)
         else:
             A.forward(p, q_out, k_out, dev["v"], o, scale, qs, ks)
@@ -342,9 +366,10 @@ def main():
     fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
     peak = mixed_peak(int8, fp8v)
     # prep: algorithmic bytes = read Q and K (bf16), write Q' and K' (+ scales in int8);
-    # with FP8 P V also read V and write its codes and channel scales
+    # with FP8 P V also read V and write its codes and channel scales; with the Q
+    # prep fused into the forward, read K and write K' only
     n, h = wl.n_tokens, wl.heads
-    prep_bytes = 2 * n * h * 128 * 2 + 2 * n * h * 128 * (1 if int8 else 2) + \
+    prep_bytes = (1 if fused else 2) * n * h * 128 * 2 + (1 if fused else 2) * n * h * 128 * (1 if int8 else 2) + \
         (2 * h * ((n + 63) // 64) * 4 if int8 else 0) + \
         (n * h * 128 * 3 + h * 128 * 4 if fp8v else 0)
     dtype = "bf16" if not (int8 or fp8v) else f"{'int8' if int8 else 'bf16'}-qk/{'fp8' if fp8v else 'bf16'}-pv"
@@ -364,13 +389,14 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V, gamma ~ N(1,0.1))",
         "config": {"workload": wl.name, "n_tokens": n, "heads": h, "head_dim": 128, "batch": 1,
                    "video_grid": list(wl.grid), "audio_tokens": wl.audio, "text_tokens": wl.text,
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu", "q_prep": "fused into the forward" if fused else "separate"},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kernels": {"prep_ms": round(prep_ms, 4), "forward_ms": round(fwd_ms, 4),
                     "prep_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)},
-        "roofline": {"bound": "mfma", "kernel": "h3attn_forward", "achieved": round(fwd_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "h3attn_forward_fused_q" if fused else "h3attn_forward",
+                     "achieved": round(fwd_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(fwd_tflops / peak, 4),
-                     "traffic": forward_traffic(wl.name) if not (int8 or fp8v) else None,
+                     "traffic": forward_traffic(wl.name, fused) if not (int8 or fp8v) else None,
                      "algorithmic_bytes": 4 * n * h * 128 * 2},
     }
     if not (int8 or fp8v):
@@ -383,7 +409,7 @@ def main():
     res["kernels"]["forward_ms_min"] = round(min(fwd_all), 4)
     res["kernels"]["forward_ms_max"] = round(max(fwd_all), 4)
     res["kernels"]["forward_ms_median"] = round(sorted(fwd_all)[len(fwd_all) // 2], 4)
-    if not args.headline_only and args.config is None and not (int8 or fp8v):
+    if not args.headline_only and args.config is None and fused:
         res["per_config"] = sweep(A, W, dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
