@@ -393,7 +393,8 @@ def main():
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kernels": {"prep_ms": round(prep_ms, 4), "forward_ms": round(fwd_ms, 4),
                     "prep_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)},
-        "roofline": {"bound": "mfma", "kernel": "h3attn_forward_fused_q" if fused else "h3attn_forward",
+        "roofline": {"bound": "mfma",
+                     "kernel": "h3attn_forward_fused_q" if fused else "h3attn_forward_fp8v" if fp8v else "h3attn_forward",
                      "achieved": round(fwd_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(fwd_tflops / peak, 4),
                      "traffic": forward_traffic(wl.name, fused) if not (int8 or fp8v) else None,
