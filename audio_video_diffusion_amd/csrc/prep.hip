@@ -205,7 +205,7 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
                 aq = fmaxf(aq, red[h & 1][0][w]);
                 ak = fmaxf(ak, red[h & 1][1][w]);
             }
-            // IEEE fp32 divisions (correctly rounded: no fast-math in this build)
+            // IEEE fp32 divisions (correctly rounded: the library is compiled without fast-math)
             const float sq = aq / 127.0f, sk = ak / 127.0f;
             const float iq = aq > 0.f ? 127.0f / aq : 0.f;
             const float ik = ak > 0.f ? 127.0f / ak : 0.f;
@@ -249,7 +249,7 @@ __global__ void __launch_bounds__(256) ksum_reduce(const float* sums, float* mea
         for (int u = 0; u < 16; ++u) acc += v[u];
     }
     for (; b < nblk; ++b) acc += s[(int64_t)b * kHeadDim];
-    mean[i] = acc / (float)n;       // IEEE division (no fast-math in this build)
+    mean[i] = acc / (float)n;       // IEEE division (the library is compiled without fast-math)
 }
 
 hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream) {
