@@ -549,7 +549,9 @@ fwd8_kernel(FwdParams P) {
         // decided exactly as before, only for the (rare) tiles where some lane's
         // sum exceeds that bound, and for the ragged last tile; P is recomputed
         // only if m was raised.  The rescale decisions, hence the results, are
-        // those of computing the max for every tile.
+        // those of computing the max for every tile, as long as the logits stay
+        // far below 2^20 in base-2 units (there fp32 rounding of m + 8 cannot
+        // move a decision across the one-unit margin).
         auto raise_max = [&]() -> bool {
             float mx = S[0][0];
 #pragma unroll
