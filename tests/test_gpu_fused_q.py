@@ -149,8 +149,8 @@ def test_fused_repeated_calls_are_deterministic():
         assert same_bits(run_fused(p, dev, k_only), first)
 
 
-def test_fused_full_workload_sampled_rows():
-    cfg = W.HEADLINE
+@pytest.mark.parametrize("cfg", [1, 2, W.HEADLINE])
+def test_fused_full_workload_sampled_rows(cfg):
     wl = W.WORKLOADS[cfg]
     print(f"    {wl.name} N={wl.n_tokens} H={wl.heads}", flush=True)
     inp = W.make_inputs(cfg)
