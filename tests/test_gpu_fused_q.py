@@ -201,3 +201,19 @@ def test_fused_block24_shape_sampled_rows():
     got = f64(fused[torch.from_numpy(rows).cuda()])
     for hh in (0, wl.heads - 1):
         check(got[:, hh, :], oracle_rows_bf16(inp, hh, rows), what=f"fused {wl.name} head {hh}")
+
+
+def test_fused_head_shard_matches_full_heads():
+    # one GPU's share of the heads (strided views of the full raw Q/K/V, as the
+    # bench's shard rows run it) gives bit-identical rows to the same heads of
+    # the full problem
+    import dataclasses
+    wl = W.ragged_workload(3000, 8)
+    dev = W.device_inputs(W.make_inputs(62, wl))
+    p = problem_for(wl)
+    full = run_fused(p, dev, run_prep_k(p, dev))
+    part = dataclasses.replace(wl, heads=3)
+    view = {**dev, "q": dev["q"][:, :3], "k": dev["k"][:, :3], "v": dev["v"][:, :3]}
+    ps = problem_for(part)
+    o = run_fused(ps, view, run_prep_k(ps, view))
+    assert same_bits(o, full[:, :3].contiguous())
