@@ -14,6 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libh3attn.so")
+# race-detection build of the same sources (tests only)
+SYNC_LIB = os.path.join(PKG, "libh3attn_sync.so")
 SOURCES = ("api.hip", "prep.hip", "prep_v.hip", "forward.hip", "calib.hip")
 ARCH = "gfx950"
 
@@ -33,11 +35,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libh3attn.so")
 
 
-def build(verbose: bool = False, asm: bool = False) -> str:
-    """Compile every HIP source into the in-tree shared library; returns its path."""
+def _compile(out: str, defines=(), verbose: bool = False, asm: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
     if asm:
         os.makedirs(os.path.join(ROOT, "_build"), exist_ok=True)
         cmd[1:1] = ["-save-temps=cwd"]
@@ -52,8 +53,29 @@ def build(verbose: bool = False, asm: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, asm: bool = False) -> str:
+    """Compile every HIP source into the in-tree shared library, and the same
+    sources again into the race-detection build (a barrier after every LDS
+    stage of the forward, used by the tests only); returns the library path."""
+    _compile(LIB, verbose=verbose, asm=asm)
+    _compile(SYNC_LIB, defines=("H3_DEBUG_SYNC=1",), verbose=verbose)
     return LIB
+
+
+def device_asm(source: str, defines=()) -> str:
+    """gfx950 assembly of one HIP source under the library's flags (device pass only)."""
+    src = os.path.join(CSRC, source)
+    flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = [hipcc(), *flags, "--offload-device-only", "-S", *[f"-D{d}" for d in defines],
+           "-I", os.path.join(ROOT, "include"), src, "-o", "-"]
+    res = subprocess.run(cmd, cwd=CSRC, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stderr)
+    return res.stdout
 
 
 if __name__ == "__main__":

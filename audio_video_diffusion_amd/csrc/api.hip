@@ -395,7 +395,7 @@ int h3attn_calibrate_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* 
 
 int h3attn_debug_scores_i32(const h3attn_problem* p, const void* q_codes, const void* k_codes,
                             int32_t head, int32_t row0, int32_t nrows, int32_t col0, int32_t ncols,
-                            int32_t* out, void* stream) {
+                            int32_t fp8v_layout, int32_t* out, void* stream) {
     int rc = check_problem(p);
     if (rc) return rc;
     if (p->qk_format != H3ATTN_QK_I8_BLK64) return H3ATTN_E_UNSUPPORTED;
@@ -403,20 +403,27 @@ int h3attn_debug_scores_i32(const h3attn_problem* p, const void* q_codes, const 
     if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(out, 4)) return H3ATTN_E_ALIGN;
     const int64_t n = p->n_tokens;
     if (head < 0 || head >= p->n_heads || nrows < 1 || ncols < 1 || row0 < 0 || col0 < 0 ||
-        (int64_t)row0 + nrows > n || (int64_t)col0 + ncols > n)
+        (int64_t)row0 + nrows > n || (int64_t)col0 + ncols > n || (fp8v_layout != 0 && fp8v_layout != 1))
         return H3ATTN_E_SHAPE;
     const size_t in_b = h3attn_prepped_qk_bytes(p);
     const Range orng = span(out, (size_t)nrows * (size_t)ncols * sizeof(int32_t));
     if (overlap(orng, span(q_codes, in_b)) || overlap(orng, span(k_codes, in_b))) return H3ATTN_E_ALIAS;
 
-    h3::ScoreParams P{};
-    const int64_t head_off = (int64_t)head * npad_of(p) * 128;
-    P.qhead = static_cast<const uint8_t*>(q_codes) + head_off;
-    P.khead = static_cast<const uint8_t*>(k_codes) + head_off;
-    P.n = (int)n; P.npad = (int)npad_of(p);
-    P.row0 = row0; P.nrows = nrows; P.col0 = col0; P.ncols = ncols;
-    P.out = out;
-    if (h3::launch_scores_i8(P, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
+    // the int8 forward's own parameters (no scales, V or output are read)
+    h3::FwdParams P{};
+    P.q = q_codes; P.k = k_codes;
+    P.n = (int)n; P.h = p->n_heads; P.npad = (int)npad_of(p); P.nblk = (int)nblk_of(p);
+    const int tile_rows = h3::forward_tile_rows(true, fp8v_layout != 0);
+    P.qtiles = (int)((n + tile_rows - 1) / tile_rows);
+    P.s_out = out;
+    P.s_head = head; P.s_row0 = row0; P.s_nrows = nrows; P.s_col0 = col0; P.s_ncols = ncols;
+    P.s_qt0 = row0 / tile_rows;
+    P.total = (row0 + nrows - 1) / tile_rows - P.s_qt0 + 1;
+    P.per_xcd = (P.total + 7) / 8;
+    P.kt0 = col0 / 64;
+    P.kt1 = (col0 + ncols - 1) / 64;
+    if (h3::launch_scores_i8(P, fp8v_layout != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return H3ATTN_E_HIP;
     return H3ATTN_OK;
 }
 

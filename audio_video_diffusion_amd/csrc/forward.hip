@@ -43,8 +43,8 @@
 //   runs at a time on adjacent query tiles of one head, so K'/V tiles are
 //   shared through that XCD's L2 (int8 K': plain order, see the kernel).
 //
-// scores_i8_kernel is a test hook: the exact int32 Q K^T of the int8 path for
-// a window of rows and keys, computed with the same operand layout.
+// The int8 instantiations also run as the scores test hook (kScores): the
+// same Q'K'^T path, with the exact int32 scores of a window written out.
 #include <cfloat>
 #include <type_traits>
 
@@ -67,8 +67,6 @@ constexpr float kSumCheckFp8 = 200.0f;
 
 // LDS tile sizes in bytes; four stages of each are in flight
 constexpr int kStages = 4;          // LDS stages of the K'/V stream
-// K' tile of the int8 scores test hook: 64 rows of 128 bytes
-constexpr int kKTileI8 = kBN * 128;
 
 // Tile-local key held by LDS row rho: the 32x32 accumulator row order
 // (rows 8i + 4h + j) mapped so that accumulator element 8s+e of lane half h
@@ -88,15 +86,6 @@ __device__ __forceinline__ int key_of_row_f8(int rho) {
     return 32 * hh + 16 * kb + 4 * i + j;
 }
 
-// One 16-byte-per-lane global -> LDS DMA.  Issued as asm so the compiler does
-// not treat it as an LDS write it must wait for before later LDS reads: the
-// kernel's own vmcnt + barrier protocol orders every buffer's fill before use.
-__device__ __forceinline__ void dma16(const void* src, const uint8_t* lds_dst) {
-    const uint32_t dst = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_dst;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
-}
-
 // Raw buffer resource for `base` (stride 0, no range limit in practice: every
 // offset the kernel forms is inside the tensor).  Word 3 selects the 32-bit
 // data format that gfx9 buffer loads need.
@@ -112,31 +101,24 @@ __device__ __forceinline__ u32x4 raw_rsrc(const void* base) {
 
 // One 16-byte-per-lane buffer -> LDS DMA: lane i's 16 bytes at rsrc + voff land
 // at lds_dst + 16 i.  The per-lane offsets stay in registers for the whole
-// kernel; only the scalar base moves from tile to tile.
+// kernel; only the scalar base moves from tile to tile.  Issued as asm so the
+// compiler does not treat it as an LDS write it must wait for before later
+// LDS reads: the kernel's own vmcnt + barrier protocol orders every stage's
+// fill before its use.  M0 holds the LDS destination, and an LDS DMA reads M0
+// one wait state after a scalar write to it (the compiler's own lowering of
+// the buffer -> LDS builtin places the same s_nop 0 there): without it the
+// load may take the previous M0 and land on the previous destination.
+// The M0 clobber is declared so that the compiler keeps nothing of its own in
+// M0 across the DMA; clang warns that M0 is a reserved register, which is
+// exactly why it must be declared, so that one warning is silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16_buf(const u32x4& rsrc, uint32_t voff, const uint8_t* lds_dst) {
     const uint32_t dst = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_dst;
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
 }
-
-// ---- K' tile of the scores test hook: global -> LDS directly ---------------
-
-// Slot c of LDS row rho holds 16-byte chunk c ^ (rho mod chunks-per-row) of the
-// row's key: lanes reading one chunk of 8 (16) consecutive rows hit distinct banks.
-__device__ __forceinline__ void k_tile_async(const uint8_t* khead, int key0, uint8_t* kbuf, int wave,
-                                             int lane) {
-    constexpr int rowB = 128;                // int8 K' row
-    constexpr int cpr = rowB / 16;          // chunks per row
-    constexpr int rpi = 64 / cpr;           // rows per wave instruction
-#pragma unroll
-    for (int r = 0; r < 16 / rpi; ++r) {    // each wave fills 16 rows
-        const int row0 = 16 * wave + rpi * r;
-        const int rho = row0 + lane / cpr;
-        const int c = (lane % cpr) ^ (rho & (cpr - 1));
-        const uint8_t* src = khead + (int64_t)(key0 + key_of_row(rho)) * rowB + c * 16;
-        dma16(src, kbuf + row0 * rowB);
-    }
-}
+#pragma clang diagnostic pop
 
 // ---- S^T = K' Q'^T ---------------------------------------------------------
 
@@ -167,32 +149,6 @@ __device__ __forceinline__ void mfma_s_i8(i32x16& d, const i32x4& a, const i32x4
         asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c0));
     else
         asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
-}
-
-__device__ __forceinline__ void qk_tile(const uint8_t* kbuf, const i32x4 (&q)[2][4], i32x16 (&S)[2][2],
-                                        int n32, int hh) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        S[kb][0] = i32x16{};
-        S[kb][1] = i32x16{};
-        const int rho = 32 * kb + n32;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int slot = (2 * t + hh) ^ (rho & 7);
-            const i32x4 a = *reinterpret_cast<const i32x4*>(kbuf + rho * 128 + slot * 16);
-            S[kb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, q[0][t], S[kb][0], 0, 0, 0);
-            S[kb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, q[1][t], S[kb][1], 0, 0, 0);
-        }
-    }
-}
-
-// int8 Q' codes of one wave's 64 rows as MFMA B operands: lane (n32, hh) holds row q0+32qb+n32.
-__device__ __forceinline__ void load_q(const uint8_t* qhead, int q0, int n32, int hh, i32x4 (&q)[2][4]) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            q[qb][t] = __builtin_bit_cast(i32x4, ld16(qhead + (int64_t)(q0 + 32 * qb + n32) * 128 + 32 * t + 16 * hh));
 }
 
 // Tile-local key of accumulator element e of block kb for lane half hh.
@@ -240,6 +196,23 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Race-detection build (compiled with -DH3_DEBUG_SYNC=1 into a separate
+// library): every LDS stage of the tile loop -- the buffer -> LDS fill, the
+// K' operand reads, the V operand reads -- is closed by a wait for all of the
+// wave's memory traffic and a work-group barrier, so no stage can overlap
+// another.  Its outputs must equal the release build's bit for bit; a
+// difference would expose an ordering the release protocol leaves open.
+#ifndef H3_DEBUG_SYNC
+#define H3_DEBUG_SYNC 0
+#endif
+constexpr bool kDebugSync = H3_DEBUG_SYNC != 0;
+__device__ __forceinline__ void debug_stage_sync() {
+    if constexpr (kDebugSync) {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+}
 // Wait until at most kOutstanding of this wave's DMA instructions are still in
 // flight (vmcnt retires in issue order): with the two newest fetches allowed
 // outstanding, every older tile has landed.
@@ -250,36 +223,8 @@ __device__ __forceinline__ void wait_vmem_upto() {
     else if constexpr (kOutstanding == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else if constexpr (kOutstanding == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     else if constexpr (kOutstanding == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-__global__ void __launch_bounds__(256) scores_i8_kernel(ScoreParams P) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kKTileI8];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n32 = lane & 31, hh = lane >> 5;
-    const int qbase = (P.row0 / kBM) * kBM + blockIdx.y * kBM;
-    const int kbase = (P.col0 / kBN) * kBN + blockIdx.x * kBN;
-    const int q0 = qbase + wave * 64;
-
-    i32x4 q[2][4];
-    load_q(P.qhead, q0, n32, hh, q);
-    k_tile_async(P.khead, kbase, lds, wave, lane);
-    wait_vmem_all();
-    __syncthreads();
-    i32x16 S[2][2];
-    qk_tile(lds, q, S, n32, hh);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int qrow = q0 + 32 * qb + n32;
-                const int key = kbase + key_of_elem(kb, e, hh);
-                const int r = qrow - P.row0, c = key - P.col0;
-                if (r >= 0 && r < P.nrows && c >= 0 && c < P.ncols)
-                    P.out[(int64_t)r * P.ncols + c] = S[kb][qb][e];
-            }
+    else if constexpr (kOutstanding == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else static_assert(kOutstanding == 2, "no vmcnt wait for this count");
 }
 
 // ============================================================================
@@ -350,16 +295,23 @@ constexpr float kPLog2Fp8 = 0.8f;
 // SIMD drift out of phase and one's softmax covers the other's matrix-core
 // phases, also at the tile edges where the eight-wave form keeps them in step;
 // each row's arithmetic is unchanged.
-template <bool kInt8, bool kFp8V, bool kFuseQ = false, int kW = 8>
+// kScores (int8 only; the test hook h3attn_debug_scores_i32): the kernel runs
+// its own Q'K'^T path -- Q' codes in registers, the K' stream with its DMA
+// offsets and LDS row permutation, the int8 product chain from the
+// magic-number start -- over the key tiles of a window of one head, and
+// writes the exact int32 scores of the window in place of the softmax and the
+// P V product (no V is fetched).
+template <bool kInt8, bool kFp8V, bool kFuseQ = false, int kW = 8, bool kScores = false>
 __global__ void __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd8_kernel(FwdParams P) {
     static_assert(!(kFuseQ && kInt8), "the fused Q prologue produces bf16 Q'");
     static_assert(kW == 8 || (kW == 4 && kInt8 && kFp8V), "four waves: int8 K' with E4M3 V only");
+    static_assert(!kScores || kInt8, "the scores hook covers the int8 Q'K'^T path");
     constexpr int kBMw = 32 * kW;                  // query rows per work-group
     using D = DmaOffsets8<kInt8, kFp8V, kW>;
     constexpr int kKTileB = kBN * D::kRowB;        // 16 KB (bf16) or 8 KB (int8)
     constexpr int kVTileB = kBN * (kFp8V ? 128 : 256);   // 8 KB (E4M3) or 16 KB (bf16)
-    constexpr int kDma8 = D::kN + D::kNV;          // DMA instructions per wave per tile
+    constexpr int kDma8 = D::kN + (kScores ? 0 : D::kNV);   // DMA instructions per wave per tile
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * (kKTileB + kVTileB)];
 
     // blockIdx -> (head, query tile).  bf16 K': XCD-aware (work-group b runs on
@@ -369,8 +321,9 @@ fwd8_kernel(FwdParams P) {
     // are half the size and the XCD-aware order missed L2 unevenly.
     const int vb = kInt8 ? (int)blockIdx.x : (blockIdx.x % kXcds) * P.per_xcd + blockIdx.x / kXcds;
     if (vb >= P.total) return;
-    const int head = vb / P.qtiles;
-    const int qt = vb % P.qtiles;
+    // scores hook: work-group b takes query tile s_qt0 + b of head s_head
+    const int head = kScores ? P.s_head : vb / P.qtiles;
+    const int qt = kScores ? P.s_qt0 + vb : vb % P.qtiles;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -423,7 +376,7 @@ fwd8_kernel(FwdParams P) {
     i32x16 bias16;
 #pragma unroll
     for (int e = 0; e < 16; ++e) bias16[e] = kI8BiasBits;
-    if constexpr (kInt8) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
+    if constexpr (kInt8 && !kScores) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
     // K block scales through the constant address space: one scalar load per
     // tile, counted by lgkmcnt.  A vector load would be waited for with
     // vmcnt(0), which also drains the buffer -> LDS prefetch.
@@ -447,18 +400,22 @@ fwd8_kernel(FwdParams P) {
     f32x16 negm = f32x16{};
 
     const int ntiles = (n + kBN - 1) / kBN;
-    const int last = ntiles - 1;
-    const bool ragged = (n % kBN) != 0;
+    // key tiles jb..last run (the scores hook: the tiles of its key window)
+    const int jb = kScores ? P.kt0 : 0;
+    const int last = kScores ? P.kt1 : ntiles - 1;
+    const bool ragged = (n % kBN) != 0 && last == ntiles - 1;
 
     const D dmo(wave, lane, P.v_st, last * kBN, n);
-    float ks_cur = kInt8 ? kscale[0] : 1.f;
+    float ks_cur = kInt8 && !kScores ? kscale[0] : 1.f;
     auto fetch = [&](int t) {
         const int kt = min(t, last);
         const u32x4 kr = raw_rsrc(khead + (int64_t)kt * kKTileB);
 #pragma unroll
         for (int r = 0; r < D::kN; ++r)
             dma16_buf(kr, dmo.k[r], kbuf(t) + (D::kRowsPW * wave + (kInt8 ? 8 : 4) * r) * D::kRowB);
-        if constexpr (kFp8V) {
+        if constexpr (kScores) {
+            // scores only: no V
+        } else if constexpr (kFp8V) {
             // pad keys of the last tile are zero codes in memory: no clamp
             const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kVTileB);
 #pragma unroll
@@ -481,8 +438,10 @@ fwd8_kernel(FwdParams P) {
 
     auto tile = [&](int j, bool masked) {
         fetch(j + 3);
+        debug_stage_sync();
         // S^T of this wave's 32 queries: S[kb] = LDS rows 32kb..32kb+31
         f32x16 S[2];
+        i32x16 Si[2];
         const uint8_t* kb_ = kbuf(j);
         if constexpr (kInt8) {
             i32x4 a[2][4];
@@ -493,7 +452,6 @@ fwd8_kernel(FwdParams P) {
                 for (int t = 0; t < 4; ++t)
                     a[kb][t] = *reinterpret_cast<const i32x4*>(kb_ + rho * 128 + (((2 * t + hh) ^ (rho & 7)) * 16));
             }
-            i32x16 Si[2];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 mfma_s_i8(Si[0], a[0][t], q[t], t == 0, bias16);
@@ -501,6 +459,7 @@ fwd8_kernel(FwdParams P) {
             }
             // wait states before the VALU reads the matrix core's results
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(Si[0]), "+v"(Si[1]));
+            debug_stage_sync();
             // the fp32 values 1.5 * 2^23 + S (kI8Bias).  Whole-vector bit casts: a
             // bit cast of a single vector element is miscompiled by this compiler
             // (every such read returns element 0).
@@ -526,183 +485,199 @@ fwd8_kernel(FwdParams P) {
                 }
             }
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]), "+v"(S[1]));
+            debug_stage_sync();
         }
-        // base-2 logit scale of this tile (int8: times the two block scales)
-        float coef = P.c;
-        if constexpr (kInt8) {
-            coef = P.c * qscale * ks_cur;
-            ks_cur = kscale[min(j + 1, last)];     // the next tile's scale, loaded a tile early
-        }
-        if (masked) {
-            // keys >= N: the most negative finite score for the max, probability 0 below
+        if constexpr (kScores) {
+            // the exact int32 scores: the accumulator ends at 0x4b400000 + S
+            // (kI8Bias), written for the window's rows and keys
+            const int r = q0 + n32 - P.s_row0;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (j * kBN + key_of<kFp8V>(kb, e, hh) >= n) S[kb][e] = -FLT_MAX;
-        }
-        // P is formed from the running max m as it stands.  The row max of the
-        // tile is only needed when m may have to be raised: a lane whose 32
-        // probabilities sum to at most kSumCheck has every P <= kSumCheck, i.e.
-        // every base-2 logit at most log2(kSumCheck) = 7 above m, one unit short
-        // of the rescale threshold.  So the max is computed, and the raise
-        // decided exactly as before, only for the (rare) tiles where some lane's
-        // sum exceeds that bound, and for the ragged last tile; P is recomputed
-        // only if m was raised.  The rescale decisions, hence the results, are
-        // those of computing the max for every tile, as long as the logits stay
-        // far below 2^20 in base-2 units (there fp32 rounding of m + 8 cannot
-        // move a decision across the one-unit margin).
-        auto raise_max = [&]() -> bool {
-            float mx = S[0][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kb][e]);
-            mx = kInt8 ? (max_halves(mx) - kI8Bias) * coef : kFuseQ ? max_halves(mx) + mch : max_halves(mx) * coef;
-            if (__any(mx > m + kRescaleLog2)) {
-                const float mm = fmaxf(m, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m - mm);
-                m = mm;
-                l *= alpha;
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) scale_acc(O[cc], alpha);
-                return true;
+                for (int e = 0; e < 16; ++e) {
+                    const int c = j * kBN + key_of<kFp8V>(kb, e, hh) - P.s_col0;
+                    if (r >= 0 && r < P.s_nrows && c >= 0 && c < P.s_ncols)
+                        P.s_out[(int64_t)r * P.s_ncols + c] = Si[kb][e] - kI8BiasBits;
+                }
+        } else {
+            // base-2 logit scale of this tile (int8: times the two block scales)
+            float coef = P.c;
+            if constexpr (kInt8) {
+                coef = P.c * qscale * ks_cur;
+                ks_cur = kscale[min(j + 1, last)];     // the next tile's scale, loaded a tile early
             }
-            return false;
-        };
-        if constexpr (kFp8V) {
-            // P' = 2^0.8 * P rounded to E4M3, 32 consecutive keys per lane half;
-            // the row sum adds the fp32 P' before rounding
-            i32x8 Pf;
-            float rs[4];
-            auto make_p = [&]() {
-                const float mb0 = m - kPLog2Fp8;
-                // int8: the score bias leaves with the max (kI8Bias)
-                const float mb = kInt8 ? __builtin_fmaf(kI8Bias, coef, mb0) : mb0;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) rs[u] = 0.f;
+            if (masked) {
+                // keys >= N: the most negative finite score for the max, probability 0 below
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int w4 = 0; w4 < 4; ++w4) {
-                        float x[4];
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int e = 4 * w4 + u;
-                            x[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mb));
-                            if (masked && j * kBN + key_of<true>(kb, e, hh) >= n) x[u] = 0.f;
-                            rs[u] += x[u];
-                        }
-                        // the first conversion fills the low half and keeps the high half of
-                        // its third operand, which the second overwrites: any live value
-                        // serves there (a constant 0 would cost a register move per word)
-                        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __float_as_int(x[0]), false);
-                        wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wd, true);
-                        Pf[4 * kb + w4] = wd;
-                    }
-            };
-            make_p();
-            float t = (rs[0] + rs[1]) + (rs[2] + rs[3]);
-            // P' carries the factor 2^0.8: 2^7.64 = 200 < 2^(7 + 0.8)
-            if (masked || __any(!(t <= kSumCheckFp8)))
-                if (raise_max()) {
-                    make_p();
-                    t = (rs[0] + rs[1]) + (rs[2] + rs[3]);
-                }
-            l += t;
-            // O^T += V^T P'^T: lane (n32, hh) reads d-row 32cc + n32, keys 32hh..32hh+31
-            const uint8_t* vb_ = vbuf(j) + v_lane_off;
-            const int s0 = ((2 * hh) ^ v_sw) * 16, s1 = ((2 * hh + 1) ^ v_sw) * 16;
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const i32x4 lo = *reinterpret_cast<const i32x4*>(vb_ + 32 * 64 * cc + s0);
-                const i32x4 hi = *reinterpret_cast<const i32x4*>(vb_ + 32 * 64 * cc + s1);
-                const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                // formats 0/0: E4M3 A and B; unit E8M0 block scales (127 = 2^0)
-                O[cc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, Pf, O[cc], 0, 0, 0, 0x7f7f7f7f, 0,
-                                                                        0x7f7f7f7f);
+                    for (int e = 0; e < 16; ++e)
+                        if (j * kBN + key_of<kFp8V>(kb, e, hh) >= n) S[kb][e] = -FLT_MAX;
             }
-        } else {
-            bf16x8 Pb[2][2];
-            float rs[2];
-            // shifted (kFuseQ, after m was raised): the scores still hold
-            // logit - mch, so m - mch more is subtracted
-            auto make_p = [&](const bool shifted) {
-                // int8: the score bias leaves with the max (kI8Bias)
-                const float mk = kInt8 ? __builtin_fmaf(kI8Bias, coef, m) : m;
-                const float off = mch - m;
-                rs[0] = rs[1] = 0.f;
+            // P is formed from the running max m as it stands.  The row max of the
+            // tile is only needed when m may have to be raised: a lane whose 32
+            // probabilities sum to at most kSumCheck has every P <= kSumCheck, i.e.
+            // every base-2 logit at most log2(kSumCheck) = 7 above m, one unit short
+            // of the rescale threshold.  So the max is computed, and the raise
+            // decided exactly as before, only for the (rare) tiles where some lane's
+            // sum exceeds that bound, and for the ragged last tile; P is recomputed
+            // only if m was raised.  The rescale decisions, hence the results, are
+            // those of computing the max for every tile, as long as the logits stay
+            // far below 2^20 in base-2 units (there fp32 rounding of m + 8 cannot
+            // move a decision across the one-unit margin).
+            auto raise_max = [&]() -> bool {
+                float mx = S[0][0];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kb][e]);
+                mx = kInt8 ? (max_halves(mx) - kI8Bias) * coef : kFuseQ ? max_halves(mx) + mch : max_halves(mx) * coef;
+                if (__any(mx > m + kRescaleLog2)) {
+                    const float mm = fmaxf(m, mx);
+                    const float alpha = __builtin_amdgcn_exp2f(m - mm);
+                    m = mm;
+                    l *= alpha;
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) scale_acc(O[cc], alpha);
+                    return true;
+                }
+                return false;
+            };
+            if constexpr (kFp8V) {
+                // P' = 2^0.8 * P rounded to E4M3, 32 consecutive keys per lane half;
+                // the row sum adds the fp32 P' before rounding
+                i32x8 Pf;
+                float rs[4];
+                auto make_p = [&]() {
+                    const float mb0 = m - kPLog2Fp8;
+                    // int8: the score bias leaves with the max (kI8Bias)
+                    const float mb = kInt8 ? __builtin_fmaf(kI8Bias, coef, mb0) : mb0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) rs[u] = 0.f;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int w4 = 0; w4 < 4; ++w4) {
+                            float x[4];
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                const int e = 4 * w4 + u;
+                                x[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mb));
+                                if (masked && j * kBN + key_of<true>(kb, e, hh) >= n) x[u] = 0.f;
+                                rs[u] += x[u];
+                            }
+                            // the first conversion fills the low half and keeps the high half of
+                            // its third operand, which the second overwrites: any live value
+                            // serves there (a constant 0 would cost a register move per word)
+                            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __float_as_int(x[0]), false);
+                            wd = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], wd, true);
+                            Pf[4 * kb + w4] = wd;
+                        }
+                };
+                make_p();
+                float t = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+                // P' carries the factor 2^0.8: 2^7.64 = 200 < 2^(7 + 0.8)
+                if (masked || __any(!(t <= kSumCheckFp8)))
+                    if (raise_max()) {
+                        make_p();
+                        t = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+                    }
+                l += t;
+                // O^T += V^T P'^T: lane (n32, hh) reads d-row 32cc + n32, keys 32hh..32hh+31
+                const uint8_t* vb_ = vbuf(j) + v_lane_off;
+                const int s0 = ((2 * hh) ^ v_sw) * 16, s1 = ((2 * hh + 1) ^ v_sw) * 16;
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    const i32x4 lo = *reinterpret_cast<const i32x4*>(vb_ + 32 * 64 * cc + s0);
+                    const i32x4 hi = *reinterpret_cast<const i32x4*>(vb_ + 32 * 64 * cc + s1);
+                    const i32x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    // formats 0/0: E4M3 A and B; unit E8M0 block scales (127 = 2^0)
+                    O[cc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, Pf, O[cc], 0, 0, 0, 0x7f7f7f7f, 0,
+                                                                            0x7f7f7f7f);
+                }
+            } else {
+                bf16x8 Pb[2][2];
+                float rs[2];
+                // shifted (kFuseQ, after m was raised): the scores still hold
+                // logit - mch, so m - mch more is subtracted
+                auto make_p = [&](const bool shifted) {
+                    // int8: the score bias leaves with the max (kI8Bias)
+                    const float mk = kInt8 ? __builtin_fmaf(kI8Bias, coef, m) : m;
+                    const float off = mch - m;
+                    rs[0] = rs[1] = 0.f;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int s = 0; s < 2; ++s) {
+                            u32x4 w;
+#pragma unroll
+                            for (int ii = 0; ii < 4; ++ii) {
+                                const int e = 8 * s + 2 * ii;
+                                float x0, x1;
+                                if constexpr (kFuseQ) {
+                                    x0 = __builtin_amdgcn_exp2f(shifted ? S[kb][e] + off : S[kb][e]);
+                                    x1 = __builtin_amdgcn_exp2f(shifted ? S[kb][e + 1] + off : S[kb][e + 1]);
+                                } else {
+                                    x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mk));
+                                    x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], coef, -mk));
+                                }
+                                if (masked) {
+                                    if (j * kBN + key_of_elem(kb, e, hh) >= n) x0 = 0.f;
+                                    if (j * kBN + key_of_elem(kb, e + 1, hh) >= n) x1 = 0.f;
+                                }
+                                const f32x2 f = {x0, x1};
+                                const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+                                rs[s] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs[s], false);
+                                w[ii] = __builtin_bit_cast(uint32_t, b);
+                            }
+                            Pb[kb][s] = __builtin_bit_cast(bf16x8, w);
+                        }
+                };
+                make_p(false);
+                float t = rs[0] + rs[1];
+                // kFuseQ: the first tile sets the running max (its chain started from 0)
+                if (masked || (kFuseQ && j == 0) || __any(!(t <= kSumCheck)))
+                    if (raise_max()) {
+                        make_p(true);
+                        t = rs[0] + rs[1];
+                        if constexpr (kFuseQ) {
+                            mch = m;
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) negm[e] = -m;
+                        }
+                    }
+                l += t;
+                // O^T += V^T P^T
+                const uint8_t* vb_ = vbuf(j);
+                typedef short i16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
-                        u32x4 w;
+                        bf16x8 a[4];
 #pragma unroll
-                        for (int ii = 0; ii < 4; ++ii) {
-                            const int e = 8 * s + 2 * ii;
-                            float x0, x1;
-                            if constexpr (kFuseQ) {
-                                x0 = __builtin_amdgcn_exp2f(shifted ? S[kb][e] + off : S[kb][e]);
-                                x1 = __builtin_amdgcn_exp2f(shifted ? S[kb][e + 1] + off : S[kb][e + 1]);
-                            } else {
-                                x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e], coef, -mk));
-                                x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][e + 1], coef, -mk));
-                            }
-                            if (masked) {
-                                if (j * kBN + key_of_elem(kb, e, hh) >= n) x0 = 0.f;
-                                if (j * kBN + key_of_elem(kb, e + 1, hh) >= n) x1 = 0.f;
-                            }
-                            const f32x2 f = {x0, x1};
-                            const bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
-                            rs[s] = __builtin_amdgcn_fdot2_f32_bf16(b, ones, rs[s], false);
-                            w[ii] = __builtin_bit_cast(uint32_t, b);
+                        for (int cc = 0; cc < 4; ++cc) {
+                            const int off = v_lane_off + 64 * (cc ^ rk) + (32 * kb + 16 * s) * 256;
+                            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) i16x4*)(vb_ + off));
+                            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) i16x4*)(vb_ + off + 4 * 256));
+                            a[cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                         }
-                        Pb[kb][s] = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+                        for (int cc = 0; cc < 4; ++cc)
+                            O[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cc], Pb[kb][s], O[cc], 0, 0, 0);
                     }
-            };
-            make_p(false);
-            float t = rs[0] + rs[1];
-            // kFuseQ: the first tile sets the running max (its chain started from 0)
-            if (masked || (kFuseQ && j == 0) || __any(!(t <= kSumCheck)))
-                if (raise_max()) {
-                    make_p(true);
-                    t = rs[0] + rs[1];
-                    if constexpr (kFuseQ) {
-                        mch = m;
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) negm[e] = -m;
-                    }
-                }
-            l += t;
-            // O^T += V^T P^T
-            const uint8_t* vb_ = vbuf(j);
-            typedef short i16x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    bf16x8 a[4];
-#pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) {
-                        const int off = v_lane_off + 64 * (cc ^ rk) + (32 * kb + 16 * s) * 256;
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(vb_ + off));
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(vb_ + off + 4 * 256));
-                        a[cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    }
-#pragma unroll
-                    for (int cc = 0; cc < 4; ++cc)
-                        O[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cc], Pb[kb][s], O[cc], 0, 0, 0);
-                }
+            }
         }
+        debug_stage_sync();
         wait_vmem_upto<2 * kDma8>();               // tile j+1 has landed
         __syncthreads();
     };
 
-    fetch(0);
-    fetch(1);
-    fetch(2);
+    fetch(jb);
+    fetch(jb + 1);
+    fetch(jb + 2);
     if constexpr (kFuseQ) {
         // Q' of the work-group's 256 rows, computed while tiles 0..2 stream
         // in, in two halves of 128 rows staged through LDS stage 3 (K' part:
@@ -745,9 +720,10 @@ fwd8_kernel(FwdParams P) {
     }
     wait_vmem_upto<2 * kDma8>();
     __syncthreads();
-    for (int j = 0; j < last; ++j) tile(j, false);
+    for (int j = jb; j < last; ++j) tile(j, false);
     tile(last, ragged);
     wait_vmem_all();
+    if constexpr (kScores) return;
     // O is complete here in every lane.  A matrix-core product reads the
     // operands (and the E4M3 path's per-lane scale registers) of all 64 lanes,
     // so none may move into the store branch below, where the lanes of rows
@@ -796,12 +772,16 @@ hipError_t launch_forward_fused_q(const FwdParams& P, hipStream_t stream) {
 
 int forward_tile_rows(bool int8, bool fp8v) { return int8 && fp8v ? 128 : kBM; }
 
-hipError_t launch_scores_i8(const ScoreParams& P, hipStream_t stream) {
+// The int8 forward's own Q'K'^T path over a window (kScores): `fp8v_layout`
+// picks the four-wave form of the E4M3-V forward (its K' row order) instead of
+// the eight-wave form.  P.total work-groups take query tiles s_qt0.. of head
+// s_head; key tiles kt0..kt1 stream through the stages.
+hipError_t launch_scores_i8(const FwdParams& P, bool fp8v_layout, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
-    const int r_lo = (P.row0 / kBM) * kBM, c_lo = (P.col0 / kBN) * kBN;
-    const int ry = (P.row0 + P.nrows - r_lo + kBM - 1) / kBM;
-    const int cx = (P.col0 + P.ncols - c_lo + kBN - 1) / kBN;
-    hipLaunchKernelGGL(scores_i8_kernel, dim3(cx, ry), dim3(256), 0, stream, P);
+    if (fp8v_layout)
+        hipLaunchKernelGGL((fwd8_kernel<true, true, false, 4, true>), dim3(P.total), dim3(256), 0, stream, P);
+    else
+        hipLaunchKernelGGL((fwd8_kernel<true, false, false, 8, true>), dim3(P.total), dim3(512), 0, stream, P);
     return hipGetLastError();
 }
 

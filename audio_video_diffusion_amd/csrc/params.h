@@ -47,14 +47,11 @@ struct FwdParams {
     int total;              // H * qtiles
     int per_xcd;            // ceil(total / 8)
     float c;                // softmax_scale * log2(e)
-};
-
-struct ScoreParams {
-    const uint8_t* qhead;   // head base of the int8 codes
-    const uint8_t* khead;
-    int n, npad;
-    int row0, nrows, col0, ncols;
-    int32_t* out;
+    // int32 scores hook only: window [s_row0, +s_nrows) x [s_col0, +s_ncols) of
+    // head s_head into s_out (row-major); query tiles s_qt0 .. s_qt0 + total - 1,
+    // key tiles kt0 .. kt1
+    int32_t* s_out;
+    int s_head, s_row0, s_nrows, s_col0, s_ncols, s_qt0, kt0, kt1;
 };
 
 hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream);
@@ -66,7 +63,8 @@ int forward_tile_rows(bool int8, bool fp8v);
 // bf16 Q'/K', V through its view, Q' computed from raw Q in the prologue
 hipError_t launch_forward_fused_q(const FwdParams& P, hipStream_t stream);
 hipError_t launch_prep_v(const PrepVParams& P, hipStream_t stream);
-hipError_t launch_scores_i8(const ScoreParams& P, hipStream_t stream);
+// the int8 forward's Q'K'^T path writing the exact int32 scores of a window
+hipError_t launch_scores_i8(const FwdParams& P, bool fp8v_layout, hipStream_t stream);
 hipError_t launch_mfma_calib(float* out, int blocks, int iters, hipStream_t stream);
 
 }  // namespace h3

@@ -19,11 +19,15 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libh3attn.so")
+# another build of the library can be bound by loading this module's source
+# under a new name with _LIB_PATH set first (see :func:`variant`)
+LIB_PATH = globals().get("_LIB_PATH", os.path.join(PKG, "libh3attn.so"))
+# the race-detection build: a barrier after every LDS stage of the forward
+SYNC_LIB_PATH = os.path.join(PKG, "libh3attn_sync.so")
 
 QK_BF16 = 0
 QK_I8_BLK64 = 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_UNSUPPORTED", -4: "E_ALIGN",
           -5: "E_ALIAS", -6: "E_HIP"}
@@ -46,6 +50,11 @@ class Problem(ctypes.Structure):
         ("rms_eps", ctypes.c_float),
         ("qk_format", ctypes.c_int32),
     ]
+
+
+# a binding bound to another build (:func:`variant`) shares this class, so the
+# same descriptor objects are accepted by both
+Problem = globals().get("_PROBLEM_CLASS", Problem)
 
 
 def problem(n_tokens: int, n_heads: int, qk_format: int = QK_BF16, head_dim: int = 128,
@@ -92,7 +101,7 @@ def _load():
                                                vp, vp, vp, vp, vp, vp]),
         "h3attn_prep_v_fp8": (ctypes.c_int, [pp, vp, i64, i64, vp, vp, vp]),
         "h3attn_forward_fp8v": (ctypes.c_int, [pp, vp, vp, vp, vp, vp, vp, vp, i64, i64, f32, vp]),
-        "h3attn_debug_scores_i32": (ctypes.c_int, [pp, vp, vp, i32, i32, i32, i32, i32, vp, vp]),
+        "h3attn_debug_scores_i32": (ctypes.c_int, [pp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]),
         "h3attn_calibrate_mfma_bf16": (ctypes.c_int, [i32, i32, vp, vp]),
         "h3attn_prep_k": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, vp, vp, vp]),
         "h3attn_forward_fused_q": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, vp, vp, vp, i64, i64, vp, i64, i64,
@@ -110,6 +119,20 @@ def _load():
 
 _lib = _load()
 lib = _lib
+
+
+def variant(path: str):
+    """This binding, bound to another build of the library (e.g. :data:`SYNC_LIB_PATH`).
+
+    Returns a separate module object whose functions call the library at
+    ``path``; this module keeps its own library."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(f"{__name__}_variant_{abs(hash(path))}", __file__)
+    mod = importlib.util.module_from_spec(spec)
+    mod._LIB_PATH = path
+    mod._PROBLEM_CLASS = Problem
+    spec.loader.exec_module(mod)
+    return mod
 
 
 def padded_tokens(p: Problem) -> int:
@@ -261,10 +284,12 @@ def forward_fp8v(p: Problem, q_prep, k_prep, v_codes, v_scales, o, softmax_scale
 
 
 def debug_scores_i32(p: Problem, q_codes, k_codes, head: int, row0: int, nrows: int, col0: int,
-                     ncols: int, out, stream=None):
-    """``h3attn_debug_scores_i32`` into ``out`` (int32 [nrows, ncols], contiguous)."""
+                     ncols: int, out, stream=None, fp8v_layout: int = 0):
+    """``h3attn_debug_scores_i32`` into ``out`` (int32 [nrows, ncols], contiguous).
+
+    ``fp8v_layout`` 1 runs the four-wave kernel of the int8 + E4M3-V forward."""
     rc = _lib.h3attn_debug_scores_i32(ctypes.byref(p), _ptr(q_codes), _ptr(k_codes), head, row0,
-                                      nrows, col0, ncols, _ptr(out), _stream(stream))
+                                      nrows, col0, ncols, fp8v_layout, _ptr(out), _stream(stream))
     if rc:
         raise H3AttnError(rc, "h3attn_debug_scores_i32")
 

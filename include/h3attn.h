@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 5
+#define H3ATTN_ABI_VERSION 6
 
 typedef enum {
     H3ATTN_OK = 0,
@@ -300,18 +300,29 @@ int h3attn_forward_fused_q(const h3attn_problem* p,
 
 /*
  * h3attn_debug_scores_i32 - test hook for the int8 format: the exact int32
- * Q'K'^T of one head over a window, computed by the same matrix-core tile
- * routine that h3attn_forward uses for its logits.
+ * Q'K'^T of one head over a window, computed by the int8 forward's own
+ * kernel ("H3 Runtime Current State", Owned Performance Kernels: the INT8 QK
+ * mainloop, held to byte-exactness there).  The kernel is h3attn_forward's
+ * int8 kernel instantiated to stop after the Q'K'^T products: the same Q'
+ * operand registers, the same buffer -> LDS stream of K' tiles with its row
+ * permutation and chunk swizzle, the same int8 matrix-core chain started from
+ * the bit pattern of 1.5 * 2^23; it writes the accumulators minus that start
+ * in place of the softmax (V is not read).
  *   out[r][c] = sum_d q_codes[head][row0 + r][d] * k_codes[head][col0 + c][d]
  * for r < nrows, c < ncols (out is int32 [nrows][ncols], row-major, device).
+ * fp8v_layout: 0 = the form h3attn_forward runs (eight waves, 256 query rows
+ *            per work-group), 1 = the form h3attn_forward_fp8v runs with int8
+ *            Q'/K' (four waves, 128 rows, the K' row order of the FP8 P V
+ *            product).
  * Requires the int8 format, 0 <= head < H, nrows, ncols >= 1,
- * 0 <= row0, row0 + nrows <= N, 0 <= col0, col0 + ncols <= N.
+ * 0 <= row0, row0 + nrows <= N, 0 <= col0, col0 + ncols <= N,
+ * fp8v_layout in {0, 1} (E_SHAPE otherwise).
  * Errors: as for h3attn_prep.
  */
 int h3attn_debug_scores_i32(const h3attn_problem* p,
                             const void* q_codes, const void* k_codes,
                             int32_t head, int32_t row0, int32_t nrows,
-                            int32_t col0, int32_t ncols,
+                            int32_t col0, int32_t ncols, int32_t fp8v_layout,
                             int32_t* out, void* stream);
 
 /* Static description of a status code (never NULL). */

@@ -65,6 +65,7 @@ __all__ = [
     "softmax_rows", "attention", "attention_head", "attention_rows_head",
     "quantize_i8", "scores_i32", "attention_i8_rows_head",
     "e4m3_bits", "e4m3_bits_to_f64", "quantize_v_fp8", "dequantize_v_fp8",
+    "FP8_P_LOG2_FACTOR", "attention_fp8v_rows",
     "k_mean_blocked", "smooth_k",
 ]
 
@@ -364,6 +365,50 @@ def quantize_v_fp8(v: np.ndarray):
 def dequantize_v_fp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """The V the FP8 P V product multiplies: code value times channel scale (float64)."""
     return e4m3_bits_to_f64(codes) * scales.astype(np.float64)[None, :]
+
+
+# log2 of the factor the FP8 P V product applies to each softmax numerator
+# before rounding it to E4M3 (reading R20 of the design notes): it cancels
+# between numerator and denominator and only moves small numerators away from
+# the subnormal range.
+FP8_P_LOG2_FACTOR = 0.8
+
+
+def attention_fp8v_rows(s: np.ndarray, v_hat: np.ndarray, p_log2_factor: float = FP8_P_LOG2_FACTOR):
+    """Reference and per-element error bound of the FP8 P V product.
+
+    The FP8-PV step of the SageAttention2 path ("H3 Runtime Current State",
+    Owned Performance Kernels: INT8 QK and FP8 PV) multiplies the softmax
+    numerators, rounded to E4M3, by the dequantised E4M3 V, and divides by the
+    sum of the unrounded numerators (softmax statistics stay in fp32 there).
+
+    ``s``: the scores of some query rows against all N keys, already times the
+    softmax scale, float64 [R, N].  ``v_hat``: the dequantised V of the head,
+    float64 [N, d] (:func:`dequantize_v_fp8`).
+
+    Returns ``(ref, bound)``, both float64 [R, d]:
+    * ref = softmax(s) @ v_hat, the exact attention over the dequantised V (the
+      result with P kept exact, as against bf16);
+    * bound: the largest change that rounding each numerator to E4M3 can make.
+      With r = softmax(s) and Z = sum_m exp(s_m - max s), the numerator of key m
+      is a * exp(s_m - m') for a = 2^p_log2_factor and some running max
+      m' <= max s, so the denominator is at least a * Z; nearest rounding to
+      E4M3 moves a numerator x by at most 2^-4 x when x is normal (3 mantissa
+      bits) and by at most 2^-10 (half the subnormal spacing 2^-9) otherwise.
+      Summed against |v_hat| this gives
+          bound = 2^-4 * r @ |v_hat| + 2^-10 / (a Z) * sum_m |v_hat_m|.
+    """
+    s = np.asarray(s, dtype=np.float64)
+    v_hat = np.asarray(v_hat, dtype=np.float64)
+    smax = s.max(axis=1, keepdims=True)
+    e = np.exp(s - smax)
+    z = e.sum(axis=1, keepdims=True)
+    r = e / z
+    av = np.abs(v_hat)
+    ref = r @ v_hat
+    a = 2.0 ** p_log2_factor
+    bound = 2.0 ** -4 * (r @ av) + 2.0 ** -10 / (a * z) * av.sum(axis=0)[None, :]
+    return ref, bound
 
 
 # ----------------------------------------------------------------------------

@@ -28,18 +28,21 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(h3attn_\w+)\s*\(", text)))
 
 
-def test_library_exports_every_declared_symbol():
+@pytest.mark.parametrize("path", [A.LIB_PATH, A.SYNC_LIB_PATH], ids=["release", "race-detection"])
+def test_library_exports_every_declared_symbol(path):
     names = declared_functions()
     assert {"h3attn_prep", "h3attn_forward", "h3attn_debug_scores_i32"} <= set(names)
-    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True).stdout
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (h3attn_\w+)", out))
+    lib = A.lib if path == A.LIB_PATH else A.variant(path).lib
     for n in names:
         assert n in exported, n
-        assert hasattr(A.lib, n)
+        assert hasattr(lib, n)
+    assert lib.h3attn_abi_version() == A.ABI_VERSION
 
 
 def test_abi_version_and_status_strings():
-    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 5
+    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 6
     for s in (0, -1, -2, -3, -4, -5, -6, 7):
         assert A.lib.h3attn_status_string(s)
 
@@ -221,14 +224,16 @@ def test_calibration_checks():
 
 def test_debug_scores_checks():
     p8 = A.problem(300, 2, A.QK_I8_BLK64)
-    call = lambda p=p8, head=0, r0=0, nr=10, c0=0, nc=10, out=K: A.lib.h3attn_debug_scores_i32(
-        ctypes.byref(p), F, G, head, r0, nr, c0, nc, out, None)
+    call = lambda p=p8, head=0, r0=0, nr=10, c0=0, nc=10, lay=0, out=K: A.lib.h3attn_debug_scores_i32(
+        ctypes.byref(p), F, G, head, r0, nr, c0, nc, lay, out, None)
     assert call(p=A.problem(300, 2)) == -3
     assert call(head=2) == -2
     assert call(head=-1) == -2
     assert call(nr=0) == -2
     assert call(r0=295, nr=6) == -2
     assert call(c0=300) == -2
+    assert call(lay=2) == -2
+    assert call(lay=-1) == -2
     assert call(out=None) == -1
     assert call(out=F + 64) == -5
 

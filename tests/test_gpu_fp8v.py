@@ -23,11 +23,11 @@ import oracle as O
 from audio_video_diffusion_amd import h3attn as A
 from audio_video_diffusion_amd import workloads as W
 
-from gpu_util import SCALE, errors, f64, problem_for, run_prep
+from gpu_util import MAX_ABS, SCALE, errors, f64, problem_for, run_prep
 
 pytestmark = pytest.mark.gpu
 
-ALPHA = 2.0 ** 0.8          # numerator factor before E4M3 rounding (cancels in the quotient)
+ALPHA = 2.0 ** O.FP8_P_LOG2_FACTOR    # numerator factor before E4M3 rounding (cancels in the quotient)
 REL_L2_FP8 = 5e-2           # stage gate (see the module docstring)
 REL_L2_FP8_E2E = 8e-2       # against fp64 with the unquantised V: P and V rounding together
 
@@ -55,24 +55,6 @@ def run_fwd8v(p, q_out, k_out, codes, scales, n, h, qs=None, ks=None):
     o = torch.empty((n, h, 128), dtype=torch.bfloat16, device="cuda")
     A.forward_fp8v(p, q_out, k_out, codes, scales, o, SCALE, qs, ks)
     return o
-
-
-def stage_rows(s, v_hat):
-    """Exact softmax rows of the scores ``s`` [r, N] (already times the softmax
-    scale) against ``v_hat`` [N, d], and the E4M3 rounding bound per element.
-
-    With Z = sum_m exp(s_m - max s), the kernel's denominator is at least
-    2^0.8 * Z, and rounding numerator m changes it by at most
-    max(2^-4 * its value, 2^-10); summed against |v| this bounds the output error.
-    """
-    smax = s.max(axis=1, keepdims=True)
-    e = np.exp(s - smax)
-    z = e.sum(axis=1, keepdims=True)
-    r = e / z
-    av = np.abs(v_hat)
-    ref = r @ v_hat
-    bound = 2.0 ** -4 * (r @ av) + 2.0 ** -10 / (ALPHA * z) * av.sum(axis=0)[None, :]
-    return ref, bound
 
 
 def check_fp8(got, ref, bound, what, rel_l2=REL_L2_FP8):
@@ -164,7 +146,7 @@ def test_forward_fp8v_matches_oracle(n, int8):
     else:
         o = run_fwd8v(p16, q16, k16, codes, vsc, N, H)
     got = f64(o)
-    refs, bounds, gots = [], [], []
+    refs, bounds, gots, vq = [], [], [], []
     for hh in range(H):
         if int8:
             cq, cs = q8[hh, :N].cpu().numpy(), qs[hh].cpu().numpy().astype(np.float64)
@@ -174,17 +156,29 @@ def test_forward_fp8v_matches_oracle(n, int8):
         else:
             qv, kv = f64(q16)[hh, :N], f64(k16)[hh, :N]
             s = (qv @ kv.T) * SCALE
-        ref, bound = stage_rows(s, v_hat_of(inp.v[:, hh, :]))
+        v_hat = v_hat_of(inp.v[:, hh, :])
+        ref, bound = O.attention_fp8v_rows(s, v_hat)
         refs.append(ref)
         bounds.append(bound)
         gots.append(got[:, hh, :])
+        # what the V quantisation alone moves each output by, on these softmax rows
+        r = O.softmax_rows(s)
+        vq.append(r @ np.abs(v_hat - O.bf16_bits_to_f64(inp.v[:, hh, :])))
     check_fp8(np.stack(gots), np.stack(refs), np.stack(bounds), what="fp8v stage")
-    # whole path against the fp64 oracle with the unquantised V
+    # whole path against the fp64 oracle with the unquantised V, per element:
+    # the P rounding bound (+ its fp32/bf16 slack), the V quantisation error on
+    # the kernel's softmax rows, and the bf16 (int8: twice the) tolerance for
+    # the rounding of Q'/K' themselves; plus the statistical gate
     qp = O.prep(inp.q, inp.gamma_q, inp.pos, W.ROPE_SECTIONS, W.ROPE_THETA, W.RMS_EPS)
     kp = O.prep(inp.k, inp.gamma_k, inp.pos, W.ROPE_SECTIONS, W.ROPE_THETA, W.RMS_EPS)
     ref64 = O.attention(qp, kp, O.bf16_bits_to_f64(inp.v), SCALE)
     mx, mn, rel = errors(got, ref64)
-    print(f"    fp8v vs fp64: max_abs={mx:.3e} mean_abs={mn:.3e} rel_l2={rel:.3e}", flush=True)
+    b = np.stack(bounds, axis=1)
+    e2e = b + 2.0 ** -8 * (np.abs(np.stack(refs, axis=1)) + b) + 1e-3 + np.stack(vq, axis=1) \
+        + (2 if int8 else 1) * MAX_ABS
+    print(f"    fp8v vs fp64: max_abs={mx:.3e} mean_abs={mn:.3e} rel_l2={rel:.3e} "
+          f"worst bound use={np.max(np.abs(got - ref64) / e2e):.3f}", flush=True)
+    assert np.all(np.abs(got - ref64) <= e2e)
     assert rel <= REL_L2_FP8_E2E, rel
 
 
@@ -205,7 +199,7 @@ def test_forward_fp8v_sharp_softmax_rescaling():
     refs, bounds = [], []
     for hh in range(wl.heads):
         qv, kv = f64(q16)[hh, :wl.n_tokens], f64(k16)[hh, :wl.n_tokens]
-        ref, bound = stage_rows((qv @ kv.T) * SCALE, v_hat_of(inp.v[:, hh, :]))
+        ref, bound = O.attention_fp8v_rows((qv @ kv.T) * SCALE, v_hat_of(inp.v[:, hh, :]))
         refs.append(ref)
         bounds.append(bound)
     check_fp8(got.transpose(1, 0, 2), np.stack(refs), np.stack(bounds), what="fp8v sharp stage")
@@ -326,7 +320,7 @@ def _sampled(wl, cfg, int8):
         else:
             qv, kv = f64(qo[hh, :N]), f64(ko[hh, :N])
             s = (qv[rows] @ kv.T) * SCALE
-        ref, bound = stage_rows(s, v_hat_of(inp.v[:, hh, :]))
+        ref, bound = O.attention_fp8v_rows(s, v_hat_of(inp.v[:, hh, :]))
         g.append(got_rows[:, hh, :])
         r.append(ref)
         b.append(bound)

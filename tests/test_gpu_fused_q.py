@@ -96,6 +96,46 @@ def test_fused_sharp_softmax_no_less_accurate_than_prep_then_forward():
     assert np.isfinite(got).all()
     for ef, ep in zip(e_fused, e_plain):
         assert ef <= 1.5 * ep + 1e-3, (e_fused, e_plain)
+    # the attention stage alone, with absolute bounds: the oracle's exact
+    # attention over the fused form's own operands -- Q'' = bf16(c * y) from the
+    # oracle's fp64 prep y with c = scale * log2(e) (logits in base 2), and the
+    # GPU's bf16 K' -- leaves only the kernel's own arithmetic (P rounded to
+    # bf16, fp32 sums, Q'' roundings that a near-tie may tip either way)
+    #
+    # The GPU forms y in fp32 (within 2^-14 |y| of the exact value), so an
+    # element of c*y closer than that to a bf16 rounding midpoint may round to
+    # the other neighbour there.  Such flips move base-2 logit m of a row by at
+    # most D_m = sum over those elements of |one bf16 spacing * k_md|, hence
+    # each softmax weight by a factor within 2^(+-2 max_m D_m), and the output
+    # by at most (2^(2 max D) - 1) * sum_m r_m |v_m|: added to the kernel's own
+    # stage bound per element.
+    c = SCALE * np.log2(np.e)
+    qp = O.prep(inp.q, inp.gamma_q, inp.pos, W.ROPE_SECTIONS, W.ROPE_THETA, W.RMS_EPS)
+    kg = f64(k_full)
+    v = O.bf16_bits_to_f64(inp.v)
+    n = wl.n_tokens
+    stage, flip = [], []
+    for hh in range(wl.heads):
+        cy = c * qp[:, hh, :]
+        qr = O.round_to_bf16(cy)
+        spacing = np.ldexp(1.0, np.floor(np.log2(np.abs(qr) + 1e-300)).astype(np.int64) - 7)
+        mid = qr + np.sign(cy - qr) * spacing / 2
+        near = np.abs(cy - mid) <= 2.0 ** -13 * np.abs(cy)
+        kh = kg[hh, :n]
+        d_max = ((near * spacing) @ np.abs(kh).T).max(axis=1)
+        s2 = qr @ kh.T
+        r = O.softmax_rows(s2 * np.log(2.0))
+        stage.append(r @ v[:, hh, :])
+        flip.append((2.0 ** (2 * d_max) - 1)[:, None] * (r @ np.abs(v[:, hh, :])))
+        print(f"    head {hh}: {near.mean():.4f} of Q'' elements near a midpoint, "
+              f"max logit shift {d_max.max():.3e}", flush=True)
+    stage = np.stack(stage, axis=1)
+    flip = np.stack(flip, axis=1)
+    err = np.abs(got - stage)
+    print(f"    fused sharp stage: max_abs={err.max():.3e} mean_abs={err.mean():.3e} "
+          f"worst (err - 1e-2) / flip bound={np.max((err - 1e-2) / np.maximum(flip, 1e-30)):.3f}", flush=True)
+    assert np.all(err <= 1e-2 + flip)
+    check(got, stage, max_abs=np.inf, rel_l2=6e-3, what="fused sharp stage")
 
 
 @pytest.mark.parametrize("sections,theta,eps", [((64, 32, 32), 500.0, 1e-5), ((16, 16, 96), 1e6, 0.0)])

@@ -63,6 +63,26 @@ def test_prep_bf16_matches_oracle(cfg, n, h, per_head):
         assert np.all(got_all[:, wl.n_tokens:, :] == 0)           # pad rows zeroed
 
 
+@pytest.mark.parametrize("cfg", [W.HEADLINE, 4])
+def test_prep_full_workload_sampled_rows(cfg):
+    # the bf16 prep at full size, every head, on sampled rows (the sequence
+    # ends, the modality boundaries, random rows; the largest positions of the
+    # grid are at its end), element by element against the oracle; pad rows zero
+    wl = W.WORKLOADS[cfg]
+    print(f"    {wl.name} N={wl.n_tokens}", flush=True)
+    inp = W.make_inputs(cfg)
+    q_out, k_out, _, _ = run_prep(problem_for(wl), W.device_inputs(inp))
+    rows = sample_rows(wl, n_random=256)
+    n = wl.n_tokens
+    for got_t, x, g in ((q_out, inp.q, inp.gamma_q), (k_out, inp.k, inp.gamma_k)):
+        got = f64(got_t[:, torch.from_numpy(rows).cuda(), :]).transpose(1, 0, 2)
+        ref = O.prep(x[rows], g, inp.pos[rows], SECTIONS, THETA, EPS)
+        err = np.abs(got - ref)
+        bound = 2.0 ** -8 * (1 + 2.0 ** -6) * np.abs(ref) + 4e-6
+        assert np.all(err <= bound), (np.max(err - bound), np.max(err))
+        assert torch.count_nonzero(got_t[:, n:, :]).item() == 0
+
+
 def test_prep_and_forward_on_interleaved_qkv_views():
     # Q/K/V as strided views of one interleaved projection output [N, 3, H, d]
     wl = W.ragged_workload(777, 3)
@@ -282,21 +302,35 @@ def test_int8_codes_and_scales_bit_exact(cfg, n, h):
             assert np.all(codes_h[hh, wl.n_tokens:] == 0)
 
 
-@pytest.mark.parametrize("cfg,n,h", [(0, None, None), (41, 4099, 2)])
+def _scores_windows(n):
+    """(row0, nrows, col0, ncols) windows: the sequence start, the end (the
+    ragged last query tile and key block), single elements and a window that
+    crosses several query tiles and key tiles."""
+    w = [(0, min(n, 300), 0, min(n, 200)), (max(0, n - 70), min(70, n), max(0, n - 130), min(130, n)),
+         (n // 3, 1, n // 2, 1), (5, min(n - 5, 250), 3, min(n - 3, 333))]
+    return [x for x in w if x[1] >= 1 and x[3] >= 1]
+
+
+def _check_scores(p8, q8, k8, heads, windows, layouts=(0, 1)):
+    for hh in heads:
+        qc = q8[hh].cpu().numpy()
+        kc = k8[hh].cpu().numpy()
+        for (r0, nr, c0, nc) in windows:
+            ref = O.scores_i32(qc[r0:r0 + nr], kc[c0:c0 + nc])
+            for lay in layouts:
+                out = torch.full((nr, nc), -1, dtype=torch.int32, device="cuda")
+                A.debug_scores_i32(p8, q8, k8, hh, r0, nr, c0, nc, out, fp8v_layout=lay)
+                assert np.array_equal(out.cpu().numpy().astype(np.int64), ref), (hh, r0, nr, c0, nc, lay)
+
+
+@pytest.mark.parametrize("cfg,n,h", [(0, None, None), (41, 4099, 2), (42, 129, 1), (43, 1, 1)])
 def test_int8_scores_i32_bit_exact(cfg, n, h):
+    # the int8 forward kernels' own Q'K'^T path (eight-wave form and the
+    # four-wave form of the E4M3-V forward) against exact integer products
     wl = W.WORKLOADS[0] if n is None else W.ragged_workload(n, h)
     inp = W.make_inputs(cfg, wl)
     _, _, p8, _, _, q8, k8, _, _ = _prep_both(wl, inp)
-    N = wl.n_tokens
-    qc, kc = q8.cpu().numpy(), k8.cpu().numpy()
-    windows = [(0, min(N, 300), 0, min(N, 200)), (max(0, N - 70), min(70, N), max(0, N - 130), min(130, N)),
-               (N // 3, 1, N // 2, 1), (5, min(N - 5, 250), 3, min(N - 3, 333))]
-    for hh in range(wl.heads):
-        for (r0, nr, c0, nc) in windows:
-            out = torch.full((nr, nc), -1, dtype=torch.int32, device="cuda")
-            A.debug_scores_i32(p8, q8, k8, hh, r0, nr, c0, nc, out)
-            ref = O.scores_i32(qc[hh, r0:r0 + nr], kc[hh, c0:c0 + nc])
-            assert np.array_equal(out.cpu().numpy().astype(np.int64), ref), (hh, r0, nr, c0, nc)
+    _check_scores(p8, q8, k8, range(wl.heads), _scores_windows(wl.n_tokens))
 
 
 @pytest.mark.parametrize("cfg,n,h", [(0, None, None), (51, 1000, 2), (52, 65, 2), (53, 4099, 2)])
@@ -335,12 +369,34 @@ def test_int8_full_workload_sampled_rows():
         r.append(oracle_rows_i8(inp, h, rows))
         g.append(got_rows[:, h, :])
     check(np.stack(g), np.stack(r), rel_l2=REL_L2_I8, what="int8 full sampled")
-    # the int32 scores of a window at the sequence end are exact
-    out = torch.empty((70, 130), dtype=torch.int32, device="cuda")
+    # the int32 scores of the forward kernels' own products are exact, on windows
+    # at the start, across query-tile and key-tile edges in the middle, and at the
+    # end, where the last key block holds 62 tokens
     n = wl.n_tokens
-    A.debug_scores_i32(p8, q8, k8, 5, n - 70, 70, n - 130, 130, out)
-    ref = O.scores_i32(q8[5, n - 70:n].cpu().numpy(), k8[5, n - 130:n].cpu().numpy())
-    assert np.array_equal(out.cpu().numpy().astype(np.int64), ref)
+    assert n % 64 == 62
+    windows = [(0, 40, 0, 70), (n // 2 - 20, 300, n // 2 - 100, 200), (n - 300, 300, n - 190, 190),
+               (n - 1, 1, 0, 64), (7, 3, n - 62, 62)]
+    _check_scores(p8, q8, k8, (5, wl.heads - 1), windows)
+
+
+def test_int8_full_workload_codes_bit_exact():
+    # the 243-frame workload's int8 codes and scales of two heads, bit-exact
+    # against the oracle's quantiser applied to the GPU's own bf16 prep output
+    cfg = 4
+    wl = W.WORKLOADS[cfg]
+    inp = W.make_inputs(cfg)
+    dev = W.device_inputs(inp)
+    n = wl.n_tokens
+    q16, k16, _, _ = run_prep(problem_for(wl), dev)
+    q8, k8, qs, ks = run_prep(problem_for(wl, int8=True), dev)
+    for hh in (0, wl.heads - 1):
+        for b16, codes, scales in ((q16, q8, qs), (k16, k8, ks)):
+            vals = f64(b16[hh])
+            c_ref, s_ref = O.quantize_i8(vals[:n].astype(np.float32))
+            assert np.array_equal(scales[hh].cpu().numpy(), s_ref), hh
+            ch = codes[hh].cpu().numpy()
+            assert np.array_equal(ch[:n], c_ref), hh
+            assert np.all(ch[n:] == 0), hh
 
 
 def test_int8_forward_is_deterministic():

@@ -516,6 +516,80 @@ def test_quantize_v_fp8_hand_cases_and_bound():
 
 
 # --------------------------------------------------------------------------
+# FP8 P V reference: its exact part against the (separately pinned) exact
+# attention and a closed form, its bound against a simulation of the rounded
+# numerators with torch's own E4M3 cast, and the bound's power to reject a
+# wrong rounding
+# --------------------------------------------------------------------------
+
+def _simulated_fp8_pv(s, v_hat, stale, cast):
+    """Numerators a * exp(s - m') with a stale running max m' = max s - stale
+    (per row), each rounded by ``cast``; divided by the unrounded sum."""
+    a = 2.0 ** O.FP8_P_LOG2_FACTOR
+    m = s.max(axis=1, keepdims=True) - stale[:, None]
+    x = a * np.exp(s - m)
+    assert x.max() < 448.0
+    return (cast(x) @ v_hat) / x.sum(axis=1, keepdims=True)
+
+
+def _torch_e4m3(x):
+    return torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_fp8v_reference_exact_part():
+    rng = np.random.default_rng(60)
+    n, d = 300, 128
+    q = rng.standard_normal((17, d))
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d)) * rng.uniform(0.1, 3, size=(1, d))
+    scale = 1 / math.sqrt(d)
+    ref, bound = O.attention_fp8v_rows((q @ k.T) * scale, v)
+    assert np.allclose(ref, O.attention_rows_head(q, k, v, scale), rtol=0, atol=1e-13)
+    assert np.all(bound > 0)
+    # equal scores: the mean of V; bound = 2^-4 mean|V| + 2^-10 / (2^0.8 N) sum|V|
+    ref, bound = O.attention_fp8v_rows(np.full((2, n), 0.7), v)
+    assert np.allclose(ref, v.mean(axis=0)[None], rtol=0, atol=1e-13)
+    expect = 2.0 ** -4 * np.abs(v).mean(axis=0) + 2.0 ** -10 / (2.0 ** 0.8 * n) * np.abs(v).sum(axis=0)
+    assert np.allclose(bound, expect[None], rtol=1e-12, atol=0)
+
+
+def test_fp8v_reference_bound_holds_for_rounded_numerators():
+    # diffuse rows, sharp rows (numerators deep in the subnormal range) and a
+    # running max up to 8 base-2 units below the true max (numerators up to 2^8 * 2^0.8)
+    rng = np.random.default_rng(61)
+    n, d = 500, 64
+    v_hat = rng.standard_normal((n, d)) * rng.uniform(0.05, 4, size=(1, d))
+    worst = 0.0
+    for spread in (0.1, 1.0, 2.0, 4.0, 8.0):
+        s = rng.standard_normal((40, n)) * spread
+        stale = rng.uniform(0, 8 * math.log(2), size=40) * (rng.uniform(size=40) < 0.5)
+        ref, bound = O.attention_fp8v_rows(s, v_hat)
+        for cast in (_torch_e4m3, lambda x: O.e4m3_bits_to_f64(O.e4m3_bits(x))):
+            sim = _simulated_fp8_pv(s, v_hat, stale, cast)
+            use = np.abs(sim - ref) / bound
+            assert np.all(use <= 1 + 1e-9), (spread, use.max())
+            worst = max(worst, float(use.max()))
+    assert worst > 0.05       # not a vacuous bound
+
+
+def test_fp8v_reference_bound_rejects_truncation():
+    # rounding toward zero (errors up to one whole spacing) must break the bound:
+    # every numerator 1.1249 truncates to 1.0
+    n, d = 64, 8
+    s = np.full((1, n), math.log(1.1249 / 2.0 ** 0.8))
+    v_hat = np.ones((n, d))
+    ref, bound = O.attention_fp8v_rows(s, v_hat)
+
+    def trunc(x):
+        e = np.floor(np.log2(x))
+        return np.floor(x / 2.0 ** (e - 3)) * 2.0 ** (e - 3)
+    sim = _simulated_fp8_pv(s, v_hat, np.zeros(1), trunc)
+    assert np.all(np.abs(sim - ref) > bound)
+    sim_ok = _simulated_fp8_pv(s, v_hat, np.zeros(1), _torch_e4m3)
+    assert np.all(np.abs(sim_ok - ref) <= bound)
+
+
+# --------------------------------------------------------------------------
 # K smoothing: the fixed-order mean, a scalar route, exactness bound,
 # softmax invariance, and its effect on the int8 quantisation error
 # --------------------------------------------------------------------------
