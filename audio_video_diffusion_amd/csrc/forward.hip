@@ -86,6 +86,18 @@ __device__ __forceinline__ int key_of_row_f8(int rho) {
     return 32 * hh + 16 * kb + 4 * i + j;
 }
 
+// 16-byte chunk c of K' row rho sits in LDS slot c ^ k_swizzle(rho) of the row.
+// An operand read (ds_read_b128) serves 16 lanes at a time, each taking 4 of
+// the 64 four-byte banks; its 16 lanes read one chunk of 16 consecutive rows.
+// bf16 rows (256 bytes) start on bank 0, so the slots of the 16 rows must
+// differ: rho & 15.  Int8 rows (128 bytes) start on bank 0 (even rows) or 32
+// (odd rows), so the slots must differ among the 8 rows of each parity:
+// (rho >> 1) & 7.  (rho & 7 would leave rows rho and rho + 8 on the same banks.)
+template <bool kInt8>
+__device__ __forceinline__ int k_swizzle(int rho) {
+    return kInt8 ? (rho >> 1) & 7 : rho & 15;
+}
+
 // Raw buffer resource for `base` (stride 0, no range limit in practice: every
 // offset the kernel forms is inside the tensor).  Word 3 selects the 32-bit
 // data format that gfx9 buffer loads need.
@@ -243,7 +255,7 @@ struct DmaOffsets8 {
 #pragma unroll
         for (int r = 0; r < kN; ++r) {
             const int rho = kRowsPW * wave + rpi * r + lane / cpr;
-            const int c = (lane % cpr) ^ (rho & (cpr - 1));
+            const int c = (lane % cpr) ^ k_swizzle<kInt8>(rho);
             k[r] = (uint32_t)((kFp8V ? key_of_row_f8(rho) : key_of_row(rho)) * kRowB + c * 16);
         }
         if constexpr (kFp8V) {
@@ -450,7 +462,7 @@ fwd8_kernel(FwdParams P) {
                 const int rho = 32 * kb + n32;
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    a[kb][t] = *reinterpret_cast<const i32x4*>(kb_ + rho * 128 + (((2 * t + hh) ^ (rho & 7)) * 16));
+                    a[kb][t] = *reinterpret_cast<const i32x4*>(kb_ + rho * 128 + (((2 * t + hh) ^ k_swizzle<true>(rho)) * 16));
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -472,7 +484,7 @@ fwd8_kernel(FwdParams P) {
                 const int rho = 32 * kb + n32;
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
-                    a[kb][t] = *reinterpret_cast<const bf16x8*>(kb_ + rho * 256 + (((2 * t + hh) ^ (rho & 15)) * 16));
+                    a[kb][t] = *reinterpret_cast<const bf16x8*>(kb_ + rho * 256 + (((2 * t + hh) ^ k_swizzle<false>(rho)) * 16));
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {

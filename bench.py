@@ -11,13 +11,25 @@ h3attn_prep then h3attn_forward (or h3attn_forward_fp8v).
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
                     [--qk bf16|int8] [--pv bf16|fp8] [--q-prep fused|separate]
                     [--headline-only]
+    python bench.py --forms [--config C] [--steps K] [--warmup W]
+    python bench.py --full-oracle
 
 Prints one JSON line.  ``value`` is attention TFLOP/s (4 N^2 d H per step)
 over the whole step; ``roofline`` rates the forward kernel alone against the
 matrix-core peak of its operand types (bf16 by default; with --qk int8 or
 --pv fp8 the harmonic mean of the two halves' rates); ``per_config`` times the
-other workloads, head shards and FP8 P V variants; ``cpu_baseline`` times the
-CPU oracle on a bounded sample of the same workload.
+other workloads, head shards and FP8 P V variants (20 calls each, 7 on the
+246,462-token workload), each beside the CPU oracle timed on an exact row
+subset of the same workload; ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the headline workload; ``gpu_clock_mhz`` is the shader clock
+sampled during the timed steps.
+
+--forms times each forward form (bf16 Q/K with the Q prep separate or fused,
+int8 Q/K, E4M3 V with bf16 or int8 Q/K) on one workload, one JSON line each:
+a short program to run under rocprofv3.  --full-oracle runs the CPU oracle
+over every row of the three smaller workloads and over a 2,048-row exact
+subset (plus the sequence ends and modality boundaries, all heads) of the two
+larger ones, on a process pool, and prints the times.
 """
 import argparse
 import json
@@ -98,6 +110,14 @@ def parse():
                          "or by h3attn_prep before h3attn_forward")
     ap.add_argument("--copy-probe", type=int, default=None, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration) and exit")
+    ap.add_argument("--forms", action="store_true",
+                    help="time each forward form on the workload (one JSON line per form) and exit")
+    ap.add_argument("--full-oracle", action="store_true",
+                    help="time the CPU oracle over whole workloads / 2,048-row subsets on a process pool and exit")
+    ap.add_argument("--sweep-steps", type=int, default=20,
+                    help="timed calls per sweep row (the 246,462-token rows take 7)")
+    ap.add_argument("--oracle-rows", type=int, default=96,
+                    help="random rows of each workload's oracle subset in the sweep")
     return ap.parse_args()
 
 
@@ -117,39 +137,117 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes_read": n * 2, "copy_probe_bytes_written": n * 2, "calls": 3}), flush=True)
 
 
-def cpu_baseline(wl, cfg, inp, rows_n, heads_n):
-    """Time the CPU oracle on `rows_n` query rows x `heads_n` heads of the workload."""
+def host_info():
+    """CPU model, core counts and the BLAS numpy calls (for the oracle timings)."""
+    info = {"cpu_count": os.cpu_count()}
+    try:
+        info["cpus_usable"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    info["cpu_model"] = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(blas[0].get("num_threads", 1))
+    except Exception:
+        pass
+    return info
+
+
+def oracle_rows(wl, n_random, seed=1234):
+    """Exact row subset of a workload for the oracle: the first 64 and last 128
+    rows, +-8 rows around each modality boundary, and `n_random` seeded rows."""
+    import numpy as np
+    n = wl.n_tokens
+    rows = set(range(min(64, n))) | set(range(max(0, n - 128), n))
+    for b in (wl.video, wl.video + wl.audio):
+        rows |= set(range(max(0, b - 8), min(n, b + 8)))
+    rng = np.random.default_rng(seed)
+    rows |= set(rng.choice(n, size=min(n_random, n), replace=False).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def oracle_operands(wl, inp, h):
+    """What every query row of head h needs from the oracle: the prep of all keys
+    and V (the int8 workload: the quantised Q'/K' of all tokens)."""
     import numpy as np
     import oracle as O
     from audio_video_diffusion_amd import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    sec, th, eps = W.ROPE_SECTIONS, W.ROPE_THETA, W.RMS_EPS
+    kp = O.prep_head(inp.k[:, h, :], inp.gamma_k, h, inp.pos, sec, th, eps)
+    ops = {"v": O.bf16_bits_to_f64(inp.v[:, h, :])}
+    if wl.qk_int8:
+        qp = O.prep_head(inp.q[:, h, :], inp.gamma_q, h, inp.pos, sec, th, eps)
+        ops["cq"], ops["sq"] = O.quantize_i8(O.round_to_bf16(qp).astype(np.float32))
+        ops["ck"], ops["sk"] = O.quantize_i8(O.round_to_bf16(kp).astype(np.float32))
+    else:
+        ops["kp"] = kp
+    return ops
+
+
+def oracle_apply(wl, inp, h, ops, rows):
+    """The oracle's output rows of head h from its operands: exact attention
+    (the int8 workload: exact integer scores of the quantised Q'/K')."""
+    import oracle as O
+    from audio_video_diffusion_amd import workloads as W
+    scale = 1.0 / math.sqrt(128.0)
+    if wl.qk_int8:
+        return O.attention_i8_rows_head(rows, ops["cq"], ops["sq"], ops["ck"], ops["sk"], ops["v"], scale)
+    qp = O.prep_head(inp.q[rows, h, :], inp.gamma_q, h, inp.pos[rows], W.ROPE_SECTIONS, W.ROPE_THETA, W.RMS_EPS)
+    return O.attention_rows_head(qp, ops["kp"], ops["v"], scale)
+
+
+def oracle_head(wl, inp, h, rows):
+    """The oracle's output rows of head h, the prep of every key included."""
+    return oracle_apply(wl, inp, h, oracle_operands(wl, inp, h), rows)
+
+
+def cpu_baseline(wl, cfg, inp, rows_n, heads_n):
+    """Time the CPU oracle on `rows_n` query rows x `heads_n` heads of the workload."""
+    import numpy as np
     n = wl.n_tokens
     rng = np.random.default_rng(1234)
     rows = np.sort(rng.choice(n, size=min(rows_n, n), replace=False))
     heads = list(range(min(heads_n, wl.heads)))
-    scale = 1.0 / math.sqrt(128.0)
-    sec, th, eps = W.ROPE_SECTIONS, W.ROPE_THETA, W.RMS_EPS
     t0 = time.perf_counter()
     for h in heads:
-        kp = O.prep_head(inp.k[:, h, :], inp.gamma_k, h, inp.pos, sec, th, eps)
-        v = O.bf16_bits_to_f64(inp.v[:, h, :])
-        if wl.qk_int8:
-            qp = O.prep_head(inp.q[:, h, :], inp.gamma_q, h, inp.pos, sec, th, eps)
-            cq, sq = O.quantize_i8(O.round_to_bf16(qp).astype(np.float32))
-            ck, sk = O.quantize_i8(O.round_to_bf16(kp).astype(np.float32))
-            O.attention_i8_rows_head(rows, cq, sq, ck, sk, v, scale)
-        else:
-            qp = O.prep_head(inp.q[rows, h, :], inp.gamma_q, h, inp.pos[rows], sec, th, eps)
-            O.attention_rows_head(qp, kp, v, scale)
+        oracle_head(wl, inp, h, rows)
     dt = time.perf_counter() - t0
     flops = 4.0 * len(rows) * n * 128 * len(heads)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    hi = host_info()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(hi.get("blas_threads", hi["cpu_count"])),
+            "kind": "oracle",
             "sample": f"{len(rows)} random query rows x {len(heads)} heads of {wl.name} (all {n} keys, "
-                      f"prep of every key included), fp64 numpy, {dt:.1f} s"}
+                      f"prep of every key included), fp64 numpy, {dt:.1f} s",
+            "seconds": round(dt, 3), "full_s_extrapolated": round(dt * n * wl.heads / (len(rows) * len(heads)), 1),
+            "host": hi}
+
+
+def oracle_subset(wl, inp, n_random, heads_n=2):
+    """Time the oracle on an exact row subset of a workload (the whole workload
+    when it is small) and extrapolate to the whole workload, labelled so."""
+    n = wl.n_tokens
+    full = n * wl.heads <= 4096
+    rows = oracle_rows(wl, n if full else n_random)
+    heads = list(range(wl.heads if full else min(heads_n, wl.heads)))
+    t0 = time.perf_counter()
+    for h in heads:
+        oracle_head(wl, inp, h, rows)
+    dt = time.perf_counter() - t0
+    frac = len(rows) * len(heads) / (n * wl.heads)
+    return {"rows": int(len(rows)), "heads": len(heads), "seconds": round(dt, 3),
+            "rows_per_s": round(len(rows) * len(heads) / dt, 1),
+            "full_s": round(dt, 3) if frac >= 1 else None,
+            "full_s_extrapolated": None if frac >= 1 else round(dt / frac, 1)}
 
 
 def mixed_peak(int8, fp8v):
@@ -158,6 +256,76 @@ def mixed_peak(int8, fp8v):
     qk = PEAK_INT8_TOPS if int8 else PEAK_BF16_TFLOPS
     pv = PEAK_FP8_TFLOPS if fp8v else PEAK_BF16_TFLOPS
     return 2.0 / (1.0 / qk + 1.0 / pv)
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock level (the starred line of the
+    driver's pp_dpm_sclk table in sysfs) from a thread while a region runs."""
+
+    def __init__(self, period_s=0.05):
+        import glob
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period_s = period_s
+        self.mhz = []
+        self._stop = None
+        self._thread = None
+
+    def _read(self):
+        import re
+        for path in self.paths:
+            try:
+                with open(path) as f:
+                    m = re.search(r"(\d+)\s*Mhz\s*\*", f.read(), re.I)
+                if m:
+                    return int(m.group(1))
+            except OSError:
+                continue
+        return None
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                v = self._read()
+                if v is not None:
+                    self.mhz.append(v)
+                self._stop.wait(self.period_s)
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        import statistics
+        if not self.mhz:
+            return None
+        return {"median": statistics.median(self.mhz), "min": min(self.mhz), "max": max(self.mhz),
+                "samples": len(self.mhz), "source": "pp_dpm_sclk (sysfs), every 50 ms over the timed steps"}
+
+
+def copy_bandwidth(mib=2048, calls=5):
+    """Device-to-device copy rate of this GPU in GB/s (bytes read + written per
+    second), timed with HIP events: the practical ceiling of an HBM-bound kernel."""
+    import torch
+    a = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        b.copy_(a)
+    e1.record()
+    e1.synchronize()
+    gbs = 2.0 * a.numel() * calls / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def mfma_sustained(A, launches=6, blocks=2048, iters=6000):
@@ -222,13 +390,16 @@ def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=No
             [b.elapsed_time(c) for _, b, c, _ in out])
 
 
-def sweep(A, W, headline_dev, steps=3, warmup=1):
+def sweep(A, W, headline_dev, steps=20, warmup=2, oracle_random=96):
     """Forward throughput of every other workload: the remaining configurations,
     the headline's per-GPU head shards, the pages' block-24 shape, and the FP8
     P V variants (V staged as E4M3) on the headline, the 243-frame int8
     workload and the block-24 shape, and the headline with the separate Q prep
-    (h3attn_prep + h3attn_forward).  The int8 Q/K + FP8 P V rows are the whole quantised path of
-    the pages, K smoothing included in their prep."""
+    (h3attn_prep + h3attn_forward).  The int8 Q/K + FP8 P V rows are the whole
+    quantised path of the pages, K smoothing included in their prep.  Each row
+    takes `steps` timed calls (7 on the 246,462-token workload) after `warmup`;
+    the first row of each workload carries the CPU oracle timed on an exact
+    row subset of it (all of it for the tiny workload)."""
     import statistics
     import torch
     scale = 1.0 / math.sqrt(128.0)
@@ -244,17 +415,20 @@ def sweep(A, W, headline_dev, steps=3, warmup=1):
     jobs += [(W.HEADLINE, hl, hl.heads, False, False, False)]
     jobs += [(100, W.BLOCK24, None, False, False, True), (100, W.BLOCK24, None, True, True, False)]
     cache = {}
+    timed_oracle = set()
     for cfg, wl, shard_heads, int8, fp8v, fused in jobs:
         print(f"[bench] sweep {wl.name}: N={wl.n_tokens} H={wl.heads} qk={'int8' if int8 else 'bf16'} "
               f"pv={'fp8' if fp8v else 'bf16'}{' q-prep fused' if fused else ''}", file=sys.stderr, flush=True)
+        inp = None
         if shard_heads is not None:
             dev = headline_dev
         else:
             if cfg not in cache:
                 cache.clear()
                 torch.cuda.empty_cache()
-                cache[cfg] = W.device_inputs(W.make_inputs(cfg, wl, threads=16))
-            dev = cache[cfg]
+                inp = W.make_inputs(cfg, wl, threads=16)
+                cache[cfg] = (inp, W.device_inputs(inp))
+            inp, dev = cache[cfg]
         fmt = A.QK_I8_BLK64 if int8 else A.QK_BF16
         p = A.problem(wl.n_tokens, wl.heads, fmt)
         q_out, k_out, qs, ks = A.alloc_prepped(p)
@@ -262,30 +436,135 @@ def sweep(A, W, headline_dev, steps=3, warmup=1):
         ksm = int8 and fp8v
         kmean = torch.empty((wl.heads, 128), dtype=torch.float32, device="cuda") if ksm else None
         o = torch.empty((wl.n_tokens, wl.heads, 128), dtype=torch.bfloat16, device="cuda")
-        prep_ms, fwd_ms, prepv_ms = time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup,
+        n_steps = 7 if wl.n_tokens > 200_000 else steps
+        prep_ms, fwd_ms, prepv_ms = time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, n_steps, warmup,
                                               shard_heads, vfp8, kmean, fused)
         med = statistics.median(fwd_ms)
         tf = wl.flops / (med * 1e-3) / 1e12
         row = {"workload": wl.name, "n_tokens": wl.n_tokens, "heads": wl.heads,
                "qk": "int8" if int8 else "bf16", "pv": "fp8" if fp8v else "bf16", "k_smoothing": ksm,
                "q_prep": "fused into the forward" if fused else "separate",
-               "steps": steps,
+               "steps": n_steps,
                "forward_ms": {"median": round(med, 4), "min": round(min(fwd_ms), 4), "max": round(max(fwd_ms), 4)},
                "prep_ms": round(statistics.median(prep_ms), 4),
                "step_ms": round(statistics.median([a + b + c for a, b, c in zip(prep_ms, fwd_ms, prepv_ms)]), 4),
-               "forward_tflops": round(tf, 2), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+               "forward_tflops": round(tf, 2)}
         if fp8v:
             row["prep_v_ms"] = round(statistics.median(prepv_ms), 4)
         if int8 or fp8v:
-            # half the work (Q K^T) at the Q/K rate, half (P V) at the P V rate
-            qk_peak = PEAK_INT8_TOPS if int8 else PEAK_BF16_TFLOPS
-            pv_peak = PEAK_FP8_TFLOPS if fp8v else PEAK_BF16_TFLOPS
-            ideal_ms = (wl.flops / 2 / (qk_peak * 1e12) + wl.flops / 2 / (pv_peak * 1e12)) * 1e3
-            row["pct_mixed_peak"] = round(100 * ideal_ms / med, 2)
+            # rated against its own ceiling: half the work (Q K^T) at the Q/K
+            # rate, half (P V) at the P V rate
+            peak = mixed_peak(int8, fp8v)
+            row["peak_tflops"] = round(peak, 1)
+            row["pct_of_peak"] = round(100 * tf / peak, 2)
+        else:
+            row["peak_tflops"] = PEAK_BF16_TFLOPS
+            row["pct_bf16_peak"] = round(100 * tf / PEAK_BF16_TFLOPS, 2)
+        if inp is not None and shard_heads is None and cfg not in timed_oracle:
+            timed_oracle.add(cfg)
+            print(f"[bench] oracle subset of {wl.name}", file=sys.stderr, flush=True)
+            orc = oracle_subset(wl, inp, oracle_random)
+            full = orc["full_s"] if orc["full_s"] is not None else orc["full_s_extrapolated"]
+            orc["gpu_speedup" if orc["full_s"] is not None else "gpu_speedup_extrapolated"] = \
+                round(full / (med * 1e-3), 1)
+            row["oracle"] = orc
         rows.append(row)
         del q_out, k_out, qs, ks, o, vfp8, kmean
         torch.cuda.empty_cache()
     return rows
+
+
+FORMS = (
+    # (name, Q/K int8, E4M3 V, Q prep fused into the forward)
+    ("bf16 Q/K, bf16 V, Q prep separate", False, False, False),
+    ("bf16 Q/K, bf16 V, Q prep fused", False, False, True),
+    ("int8 Q/K, bf16 V", True, False, False),
+    ("bf16 Q/K, E4M3 V", False, True, False),
+    ("int8 Q/K with K smoothing, E4M3 V", True, True, False),
+)
+
+
+def forms(A, W, cfg, steps, warmup):
+    """Time every forward form on workload `cfg`: one JSON line per form."""
+    import statistics
+    import torch
+    wl = W.WORKLOADS[cfg]
+    print(f"[bench] generating {wl.name}: N={wl.n_tokens} H={wl.heads}", file=sys.stderr, flush=True)
+    dev = W.device_inputs(W.make_inputs(cfg, wl, threads=16))
+    scale = 1.0 / math.sqrt(128.0)
+    for name, int8, fp8v, fused in FORMS:
+        print(f"[bench] form {name}", file=sys.stderr, flush=True)
+        p = A.problem(wl.n_tokens, wl.heads, A.QK_I8_BLK64 if int8 else A.QK_BF16)
+        q_out, k_out, qs, ks = A.alloc_prepped(p)
+        vfp8 = A.alloc_v_fp8(p) if fp8v else None
+        kmean = torch.empty((wl.heads, 128), dtype=torch.float32, device="cuda") if int8 and fp8v else None
+        o = torch.empty_like(dev["v"])
+        prep_ms, fwd_ms, prepv_ms = time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup,
+                                              None, vfp8, kmean, fused)
+        med = statistics.median(fwd_ms)
+        tf = wl.flops / (med * 1e-3) / 1e12
+        peak = mixed_peak(int8, fp8v)
+        print(json.dumps({"form": name, "workload": wl.name, "n_tokens": wl.n_tokens, "heads": wl.heads,
+                          "steps": steps, "forward_ms_median": round(med, 4), "prep_ms": round(statistics.median(prep_ms), 4),
+                          "prep_v_ms": round(statistics.median(prepv_ms), 4), "forward_tflops": round(tf, 2),
+                          "peak_tflops": round(peak, 1), "pct_of_peak": round(100 * tf / peak, 2)}), flush=True)
+        del q_out, k_out, qs, ks, o, vfp8, kmean
+        torch.cuda.empty_cache()
+
+
+_ORACLE_INPUTS = {}
+_ORACLE_HEAD = {}
+
+
+def _oracle_unit(args):
+    """One (workload, head, query block) unit of the full oracle run (process
+    pool worker).  A worker keeps the operands of the last head it prepared:
+    units arrive head by head, so each worker prepares a head's keys once."""
+    cfg, h, rows = args
+    wl, inp = _ORACLE_INPUTS[cfg]
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        if (cfg, h) not in _ORACLE_HEAD:
+            _ORACLE_HEAD.clear()
+            _ORACLE_HEAD[(cfg, h)] = oracle_operands(wl, inp, h)
+        oracle_apply(wl, inp, h, _ORACLE_HEAD[(cfg, h)], rows)
+        return time.perf_counter() - t0
+
+
+def full_oracle(W, block=256, subset_random=2048, cfgs=None):
+    """The CPU oracle over whole workloads (the three smaller ones) and over an
+    exact row subset of the two larger ones, all heads, on a process pool with
+    one BLAS thread per worker and one worker per usable core.  Each unit is one
+    head and one block of query rows; it prepares all keys of its head itself,
+    so the times include the prep.  Prints one JSON line."""
+    import multiprocessing as mp
+    import numpy as np
+    workers = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    res = {"kind": "oracle, fp64 numpy", "workers": workers, "host": host_info(), "workloads": []}
+    for cfg, wl in enumerate(W.WORKLOADS):
+        if cfgs is not None and cfg not in cfgs:
+            continue
+        inp = W.make_inputs(cfg, wl, threads=workers)
+        _ORACLE_INPUTS.clear()
+        _ORACLE_INPUTS[cfg] = (wl, inp)
+        whole = cfg < 3
+        rows = np.arange(wl.n_tokens) if whole else oracle_rows(wl, subset_random)
+        # head-major order: consecutive units of one worker share a head
+        units = [(cfg, h, rows[i:i + block]) for h in range(wl.heads) for i in range(0, len(rows), block)]
+        print(f"[oracle] {wl.name}: {len(rows)} rows x {wl.heads} heads, {len(units)} units", file=sys.stderr,
+              flush=True)
+        t0 = time.perf_counter()
+        with mp.get_context("fork").Pool(workers) as pool:
+            busy = sum(pool.map(_oracle_unit, units, chunksize=1))
+        wall = time.perf_counter() - t0
+        frac = len(rows) / wl.n_tokens
+        res["workloads"].append({
+            "workload": wl.name, "n_tokens": wl.n_tokens, "heads": wl.heads, "rows": int(len(rows)),
+            "whole": whole, "wall_s": round(wall, 1), "worker_busy_s": round(busy, 1),
+            "full_wall_s" if whole else "full_wall_s_extrapolated": round(wall / frac, 1)})
+        print(json.dumps(res["workloads"][-1]), file=sys.stderr, flush=True)
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -299,10 +578,17 @@ def main():
     if args.copy_probe is not None:
         copy_probe(args.copy_probe)
         return
+    if args.full_oracle:
+        from audio_video_diffusion_amd import workloads as W
+        full_oracle(W)
+        return
 
     import torch
     from audio_video_diffusion_amd import h3attn as A
     from audio_video_diffusion_amd import workloads as W
+    if args.forms:
+        forms(A, W, W.HEADLINE if args.config is None else args.config, args.steps, args.warmup)
+        return
 
     cfg = W.HEADLINE if args.config is None else args.config
     wl = W.WORKLOADS[cfg]
@@ -353,11 +639,12 @@ def main():
     t_start = ev()
     t_end = ev()
     torch.cuda.synchronize()
-    t_start.record()
-    for _ in range(args.steps):
-        step(timed)
-    t_end.record()
-    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        t_start.record()
+        for _ in range(args.steps):
+            step(timed)
+        t_end.record()
+        torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
     prep_ms = sum(a.elapsed_time(b) for a, b, _ in timed) / len(timed)
@@ -395,6 +682,7 @@ def main():
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kernels": {"prep_ms": round(prep_ms, 4), "forward_ms": round(fwd_ms, 4),
                     "prep_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)},
+        "gpu_clock_mhz": clock.summary(),
         "roofline": {"bound": "mfma",
                      "kernel": "h3attn_forward_fused_q" if fused else "h3attn_forward_fp8v" if fp8v else "h3attn_forward",
                      "achieved": round(fwd_tflops, 2),
@@ -408,12 +696,18 @@ def main():
         sus = mfma_sustained(A)
         res["roofline"]["sustained_peak"] = round(sus, 1)
         res["roofline"]["frac_of_sustained"] = round(fwd_tflops / sus, 4)
+    # prep is HBM-bound: its rate against the data sheet and against the copy
+    # rate this GPU sustains
+    copy_gbs = copy_bandwidth()
+    res["kernels"]["copy_GBps_measured"] = round(copy_gbs, 1)
+    res["kernels"]["prep_frac_of_copy"] = round(res["kernels"]["prep_GBps"] / copy_gbs, 3)
+    res["kernels"]["prep_frac_of_hbm_peak"] = round(res["kernels"]["prep_GBps"] / PEAK_HBM_GBS, 3)
     fwd_all = [b.elapsed_time(c) for _, b, c in timed]
     res["kernels"]["forward_ms_min"] = round(min(fwd_all), 4)
     res["kernels"]["forward_ms_max"] = round(max(fwd_all), 4)
     res["kernels"]["forward_ms_median"] = round(sorted(fwd_all)[len(fwd_all) // 2], 4)
     if not args.headline_only and args.config is None and fused:
-        res["per_config"] = sweep(A, W, dev)
+        res["per_config"] = sweep(A, W, dev, steps=args.sweep_steps, oracle_random=args.oracle_rows)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, cfg, inp, args.cpu_rows, args.cpu_heads)

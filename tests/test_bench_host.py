@@ -38,3 +38,54 @@ def test_mixed_peak_is_the_harmonic_mean_of_the_halves():
     hm = 2 / (1 / bench.PEAK_BF16_TFLOPS + 1 / bench.PEAK_FP8_TFLOPS)
     assert bench.mixed_peak(False, True) == pytest.approx(hm)
     assert bench.mixed_peak(True, True) == pytest.approx(bench.PEAK_INT8_TOPS)
+
+
+def test_oracle_rows_recipe():
+    from audio_video_diffusion_amd import workloads as W
+    wl = W.WORKLOADS[W.HEADLINE]
+    rows = bench.oracle_rows(wl, 2048)
+    n = wl.n_tokens
+    assert rows[0] == 0 and rows[-1] == n - 1 and len(set(rows.tolist())) == len(rows)
+    assert set(range(64)) <= set(rows.tolist()) and set(range(n - 128, n)) <= set(rows.tolist())
+    for b in (wl.video, wl.video + wl.audio):
+        assert set(range(b - 8, b + 8)) <= set(rows.tolist())
+    assert 2048 < len(rows) <= 2048 + 64 + 128 + 32
+    assert len(bench.oracle_rows(W.WORKLOADS[0], 10 ** 6)) == W.WORKLOADS[0].n_tokens
+
+
+def test_oracle_subset_whole_tiny_workload_and_extrapolation():
+    from audio_video_diffusion_amd import workloads as W
+    tiny = W.WORKLOADS[0]
+    r = bench.oracle_subset(tiny, W.make_inputs(0), 16)
+    assert r["full_s"] is not None and r["full_s_extrapolated"] is None
+    assert r["rows"] == tiny.n_tokens and r["heads"] == tiny.heads
+    wl = W.ragged_workload(5000, 3)
+    r = bench.oracle_subset(wl, W.make_inputs(7, wl), 32, heads_n=1)
+    assert r["full_s"] is None and r["heads"] == 1
+    assert r["full_s_extrapolated"] == pytest.approx(r["seconds"] * 5000 * 3 / r["rows"], rel=0.01)
+
+
+def test_full_oracle_mode_on_the_tiny_workload(capsys):
+    from audio_video_diffusion_amd import workloads as W
+    bench.full_oracle(W, cfgs={0})
+    import json
+    out = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert out["workloads"][0]["whole"] and out["workloads"][0]["rows"] == W.WORKLOADS[0].n_tokens
+    assert out["workers"] >= 1 and "cpu_count" in out["host"]
+
+
+def test_clock_sampler_reads_the_starred_level(tmp_path):
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 2400Mhz *\n")
+    c = bench.ClockSampler(period_s=0.01)
+    c.paths = [str(f)]
+    with c:
+        import time
+        time.sleep(0.05)
+    sm = c.summary()
+    assert sm["median"] == 2400 and sm["samples"] >= 1
+    c2 = bench.ClockSampler()
+    c2.paths = [str(tmp_path / "missing")]
+    with c2:
+        pass
+    assert c2.summary() is None
