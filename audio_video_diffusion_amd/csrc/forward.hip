@@ -125,10 +125,11 @@ __device__ __forceinline__ u32x4 raw_rsrc(const void* base) {
 // exactly why it must be declared, so that one warning is silenced here.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16_buf(const u32x4& rsrc, uint32_t voff, const uint8_t* lds_dst) {
-    const uint32_t dst = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_dst;
+// lds_dst is the destination's LDS byte address (an integer, so that no
+// generic-to-LDS pointer conversion with its null check is made per copy).
+__device__ __forceinline__ void dma16_buf(const u32x4& rsrc, uint32_t voff, uint32_t lds_dst) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(dst)) : "memory", "m0");
+                 :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_dst)) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -226,17 +227,12 @@ __device__ __forceinline__ void debug_stage_sync() {
     }
 }
 // Wait until at most kOutstanding of this wave's DMA instructions are still in
-// flight (vmcnt retires in issue order): with the two newest fetches allowed
+// flight (vmcnt retires in issue order): with the newest fetches allowed
 // outstanding, every older tile has landed.
 template <int kOutstanding>
 __device__ __forceinline__ void wait_vmem_upto() {
-    if constexpr (kOutstanding == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if constexpr (kOutstanding == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else if constexpr (kOutstanding == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if constexpr (kOutstanding == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if constexpr (kOutstanding == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if constexpr (kOutstanding == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    else static_assert(kOutstanding == 2, "no vmcnt wait for this count");
+    static_assert(kOutstanding >= 0 && kOutstanding <= 16, "no vmcnt wait for this count");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kOutstanding) : "memory");
 }
 
 // ============================================================================
@@ -324,6 +320,20 @@ fwd8_kernel(FwdParams P) {
     constexpr int kKTileB = kBN * D::kRowB;        // 16 KB (bf16) or 8 KB (int8)
     constexpr int kVTileB = kBN * (kFp8V ? 128 : 256);   // 8 KB (E4M3) or 16 KB (bf16)
     constexpr int kDma8 = D::kN + (kScores ? 0 : D::kNV);   // DMA instructions per wave per tile
+    // Staggered barrier (bf16 Q'/K' with E4M3 V only): waves 4..7 take the
+    // per-tile barrier between their softmax and their P V product instead of
+    // after it, so after each barrier they run P V of tile j while waves 0..3
+    // start Q'K'^T of tile j + 1: the two waves of each SIMD stay half a tile
+    // apart.  Each row's arithmetic is unchanged (outputs bit-identical).  A
+    // lagging wave still reads V of tile j after the barrier that ends tile j,
+    // so the stage of tile j may only be refilled after the next barrier:
+    // tiles are fetched two ahead instead of three.  Same process and box,
+    // 129,410 tokens: bf16 Q'/K' with E4M3 V -2.8%; the bf16-V forms were
+    // slower this way (bf16 +5.1%, fused Q prep +4.0%, int8 Q'/K' +1.2%) and
+    // keep the common barrier.
+    constexpr bool kStagger = kW == 8 && kFp8V && !kInt8 && !kScores;
+    // tiles fetched ahead of the one being computed
+    constexpr int kAhead = kStagger ? 2 : 3;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * (kKTileB + kVTileB)];
 
     // blockIdx -> (head, query tile).  bf16 K': XCD-aware (work-group b runs on
@@ -349,6 +359,10 @@ fwd8_kernel(FwdParams P) {
                                  : reinterpret_cast<const uint8_t*>(P.v + (int64_t)head * P.v_sh);
     auto kbuf = [&](int j) { return lds + (j % kStages) * kKTileB; };
     auto vbuf = [&](int j) { return lds + kStages * kKTileB + (j % kStages) * kVTileB; };
+    // the same stages as LDS byte addresses, for the copies' M0
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+    auto kbuf_addr = [&](int j) { return lds_addr + (uint32_t)((j % kStages) * kKTileB); };
+    auto vbuf_addr = [&](int j) { return lds_addr + (uint32_t)(kStages * kKTileB + (j % kStages) * kVTileB); };
 
     // this wave's 32 query rows as MFMA B operands
     using QOp = typename std::conditional<kInt8, i32x4, bf16x8>::type;
@@ -424,20 +438,20 @@ fwd8_kernel(FwdParams P) {
         const u32x4 kr = raw_rsrc(khead + (int64_t)kt * kKTileB);
 #pragma unroll
         for (int r = 0; r < D::kN; ++r)
-            dma16_buf(kr, dmo.k[r], kbuf(t) + (D::kRowsPW * wave + (kInt8 ? 8 : 4) * r) * D::kRowB);
+            dma16_buf(kr, dmo.k[r], kbuf_addr(t) + (D::kRowsPW * wave + (kInt8 ? 8 : 4) * r) * D::kRowB);
         if constexpr (kScores) {
             // scores only: no V
         } else if constexpr (kFp8V) {
             // pad keys of the last tile are zero codes in memory: no clamp
             const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kVTileB);
 #pragma unroll
-            for (int r = 0; r < D::kNV; ++r) dma16_buf(vr, dmo.v[r], vbuf(t) + 1024 * (D::kNV * wave + r));
+            for (int r = 0; r < D::kNV; ++r) dma16_buf(vr, dmo.v[r], vbuf_addr(t) + 1024 * (D::kNV * wave + r));
         } else {
             const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kBN * P.v_st * 2);
             const bool lt = kt == last;
 #pragma unroll
             for (int r = 0; r < 2; ++r)
-                dma16_buf(vr, lt ? dmo.vlast[r] : dmo.v[r], vbuf(t) + (8 * wave + 4 * r) * 256);
+                dma16_buf(vr, lt ? dmo.vlast[r] : dmo.v[r], vbuf_addr(t) + (8 * wave + 4 * r) * 256);
         }
     };
 
@@ -448,8 +462,16 @@ fwd8_kernel(FwdParams P) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
+    // the end of a tile: this wave's copies of tile j + 1 have landed, then
+    // the work-group barrier (after it, tile j + 1 is complete in LDS)
+    auto tile_sync = [&]() {
+        debug_stage_sync();
+        wait_vmem_upto<(kAhead - 1) * kDma8>();
+        __syncthreads();
+    };
+    const bool behind = kStagger && wave >= 4;
     auto tile = [&](int j, bool masked) {
-        fetch(j + 3);
+        fetch(j + kAhead);
         debug_stage_sync();
         // S^T of this wave's 32 queries: S[kb] = LDS rows 32kb..32kb+31
         f32x16 S[2];
@@ -595,6 +617,7 @@ fwd8_kernel(FwdParams P) {
                         t = (rs[0] + rs[1]) + (rs[2] + rs[3]);
                     }
                 l += t;
+                if (behind) tile_sync();
                 // O^T += V^T P'^T: lane (n32, hh) reads d-row 32cc + n32, keys 32hh..32hh+31
                 const uint8_t* vb_ = vbuf(j) + v_lane_off;
                 const int s0 = ((2 * hh) ^ v_sw) * 16, s1 = ((2 * hh + 1) ^ v_sw) * 16;
@@ -659,6 +682,7 @@ fwd8_kernel(FwdParams P) {
                         }
                     }
                 l += t;
+                if (behind) tile_sync();
                 // O^T += V^T P^T
                 const uint8_t* vb_ = vbuf(j);
                 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -682,14 +706,12 @@ fwd8_kernel(FwdParams P) {
                     }
             }
         }
-        debug_stage_sync();
-        wait_vmem_upto<2 * kDma8>();               // tile j+1 has landed
-        __syncthreads();
+        if (!behind) tile_sync();
     };
 
     fetch(jb);
     fetch(jb + 1);
-    fetch(jb + 2);
+    if constexpr (kAhead == 3) fetch(jb + 2);
     if constexpr (kFuseQ) {
         // Q' of the work-group's 256 rows, computed while tiles 0..2 stream
         // in, in two halves of 128 rows staged through LDS stage 3 (K' part:
@@ -730,7 +752,7 @@ fwd8_kernel(FwdParams P) {
             __syncthreads();
         }
     }
-    wait_vmem_upto<2 * kDma8>();
+    wait_vmem_upto<(kAhead - 1) * kDma8>();
     __syncthreads();
     for (int j = jb; j < last; ++j) tile(j, false);
     tile(last, ragged);
