@@ -48,21 +48,23 @@ PEAK_HBM_GBS = 8000.0
 
 # HBM bytes per launch of the forward kernel the bf16 step runs
 # (h3attn_forward_fused_q) on the 1344x768/124-frame workload, from two
-# rocprofv3 --pmc passes over one bench step (FETCH_SIZE, then WRITE_SIZE, KiB
-# per dispatch).  Each is scaled by what the same counter reports for a plain
-# 1 GiB device copy (bench.py --copy-probe 1024).  The figure belongs to the
-# kernel sources it was taken on: when csrc/forward.hip + csrc/rope_norm.h no
-# longer hash to `source_sha256`, traffic is null.  (The hash was moved once,
-# for a comment-only edit of forward.hip that left the generated code
-# instruction for instruction the same.)
+# rocprofv3 --pmc passes over `bench.py --forms --config 3` (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch, the mean of its three dispatches).  Each is
+# scaled by what the same counter reports for a plain 1 GiB device copy
+# (bench.py --copy-probe 1024).  The figure belongs to the kernel sources it
+# was taken on: when csrc/forward.hip + csrc/rope_norm.h no longer hash to
+# `source_sha256`, traffic is null.  The read figure is the L2 misses of the
+# K'/V stream, which each 256-query work-group reads whole: it depends on how
+# closely the work-groups of an XCD stay in step (the same kernel has read
+# 27 GB per launch in other builds, at the same speed).
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
     "kernel": "h3attn_forward_fused_q",
-    "source_sha256": "d4064d81eb8dc837075d520a5c0c08abe777931d193a53e6a8dfeec707715980",
-    # the copy's kernel reads 524,309 KiB per 1 GiB as FETCH_SIZE (factor 2.0) and
+    "source_sha256": "66aec44030ef15f2983bf2a2fff1ce3aeef036a94ad84d5ffd54d54fbdd9556a",
+    # the copy's kernel reads 524,319 KiB per 1 GiB as FETCH_SIZE (factor 2.0) and
     # writes 1,048,576 KiB as WRITE_SIZE (factor 1.0)
-    "fetch_kib": 13507449.6, "fetch_scale": 2.0,
-    "write_kib": 778098.2, "write_scale": 1.0,
+    "fetch_kib": 68524297.0, "fetch_scale": 2.0,
+    "write_kib": 776660.0, "write_scale": 1.0,
 }
 
 
@@ -218,18 +220,35 @@ def cpu_baseline(wl, cfg, inp, rows_n, heads_n):
     rng = np.random.default_rng(1234)
     rows = np.sort(rng.choice(n, size=min(rows_n, n), replace=False))
     heads = list(range(min(heads_n, wl.heads)))
-    t0 = time.perf_counter()
-    for h in heads:
-        oracle_head(wl, inp, h, rows)
-    dt = time.perf_counter() - t0
+    prep_s, rows_s = _timed_heads(wl, inp, heads, rows)
+    dt = prep_s + rows_s
     flops = 4.0 * len(rows) * n * 128 * len(heads)
     hi = host_info()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(hi.get("blas_threads", hi["cpu_count"])),
             "kind": "oracle",
             "sample": f"{len(rows)} random query rows x {len(heads)} heads of {wl.name} (all {n} keys, "
                       f"prep of every key included), fp64 numpy, {dt:.1f} s",
-            "seconds": round(dt, 3), "full_s_extrapolated": round(dt * n * wl.heads / (len(rows) * len(heads)), 1),
+            "seconds": round(dt, 3), "full_s_extrapolated": round(_extrapolate(wl, heads, rows, prep_s, rows_s), 1),
             "host": hi}
+
+
+def _timed_heads(wl, inp, heads, rows):
+    """Oracle time over `heads`: (prep of the heads' keys, the rows' attention)."""
+    prep_s = rows_s = 0.0
+    for h in heads:
+        t0 = time.perf_counter()
+        ops = oracle_operands(wl, inp, h)
+        t1 = time.perf_counter()
+        oracle_apply(wl, inp, h, ops, rows)
+        prep_s += t1 - t0
+        rows_s += time.perf_counter() - t1
+    return prep_s, rows_s
+
+
+def _extrapolate(wl, heads, rows, prep_s, rows_s):
+    """Whole-workload oracle time from a sample: the per-head prep of all keys
+    once per head, the attention in proportion to the rows."""
+    return wl.heads * (prep_s / len(heads) + rows_s / len(heads) * wl.n_tokens / len(rows))
 
 
 def oracle_subset(wl, inp, n_random, heads_n=2):
@@ -239,15 +258,12 @@ def oracle_subset(wl, inp, n_random, heads_n=2):
     full = n * wl.heads <= 4096
     rows = oracle_rows(wl, n if full else n_random)
     heads = list(range(wl.heads if full else min(heads_n, wl.heads)))
-    t0 = time.perf_counter()
-    for h in heads:
-        oracle_head(wl, inp, h, rows)
-    dt = time.perf_counter() - t0
-    frac = len(rows) * len(heads) / (n * wl.heads)
-    return {"rows": int(len(rows)), "heads": len(heads), "seconds": round(dt, 3),
+    prep_s, rows_s = _timed_heads(wl, inp, heads, rows)
+    dt = prep_s + rows_s
+    return {"rows": int(len(rows)), "heads": len(heads), "seconds": round(dt, 3), "prep_s": round(prep_s, 3),
             "rows_per_s": round(len(rows) * len(heads) / dt, 1),
-            "full_s": round(dt, 3) if frac >= 1 else None,
-            "full_s_extrapolated": None if frac >= 1 else round(dt / frac, 1)}
+            "full_s": round(dt, 3) if full else None,
+            "full_s_extrapolated": None if full else round(_extrapolate(wl, heads, rows, prep_s, rows_s), 1)}
 
 
 def mixed_peak(int8, fp8v):
@@ -512,58 +528,86 @@ def forms(A, W, cfg, steps, warmup):
         torch.cuda.empty_cache()
 
 
-_ORACLE_INPUTS = {}
 _ORACLE_HEAD = {}
 
 
+def _head_inputs(cfg, wl, h):
+    """Head h of workload `cfg`'s seeded inputs alone (each head has its own seed
+    stream), as a one-head Inputs."""
+    from audio_video_diffusion_amd import workloads as W
+    n = wl.n_tokens
+    one = lambda t: W.normal_head_bits(cfg, t, h, n)[:, None, :]
+    return W.Inputs(q=one(W.T_Q), k=one(W.T_K), v=one(W.T_V), gamma_q=W.gamma_bits(cfg, W.T_GAMMA_Q),
+                    gamma_k=W.gamma_bits(cfg, W.T_GAMMA_K), pos=W.positions(wl.grid, wl.audio, wl.text))
+
+
 def _oracle_unit(args):
-    """One (workload, head, query block) unit of the full oracle run (process
-    pool worker).  A worker keeps the operands of the last head it prepared:
-    units arrive head by head, so each worker prepares a head's keys once."""
+    """One (workload, head, query block) unit of the full oracle run (a worker of
+    a process pool started clean).  A worker regenerates and prepares the head
+    it is given and keeps it for the next unit: units arrive head by head."""
     cfg, h, rows = args
-    wl, inp = _ORACLE_INPUTS[cfg]
     from threadpoolctl import threadpool_limits
+    from audio_video_diffusion_amd import workloads as W
+    wl = W.WORKLOADS[cfg]
     with threadpool_limits(1):
         t0 = time.perf_counter()
-        if (cfg, h) not in _ORACLE_HEAD:
+        fresh = (cfg, h) not in _ORACLE_HEAD
+        if fresh:
             _ORACLE_HEAD.clear()
-            _ORACLE_HEAD[(cfg, h)] = oracle_operands(wl, inp, h)
-        oracle_apply(wl, inp, h, _ORACLE_HEAD[(cfg, h)], rows)
-        return time.perf_counter() - t0
+            inp = _head_inputs(cfg, wl, h)
+            _ORACLE_HEAD[(cfg, h)] = (inp, oracle_operands(wl, inp, 0))
+        t1 = time.perf_counter()
+        inp, ops = _ORACLE_HEAD[(cfg, h)]
+        oracle_apply(wl, inp, 0, ops, rows)
+        return t1 - t0, time.perf_counter() - t1, fresh
 
 
 def full_oracle(W, block=256, subset_random=2048, cfgs=None):
     """The CPU oracle over whole workloads (the three smaller ones) and over an
     exact row subset of the two larger ones, all heads, on a process pool with
     one BLAS thread per worker and one worker per usable core.  Each unit is one
-    head and one block of query rows; it prepares all keys of its head itself,
-    so the times include the prep.  Prints one JSON line."""
+    head and one block of query rows; a worker prepares all keys of a head the
+    first time it gets one of its units, so the times include the prep.  The
+    workers start as fresh interpreters (no threads inherited) and regenerate
+    their heads' inputs from the seeds.  Prints one JSON line."""
     import multiprocessing as mp
     import numpy as np
     workers = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     res = {"kind": "oracle, fp64 numpy", "workers": workers, "host": host_info(), "workloads": []}
-    for cfg, wl in enumerate(W.WORKLOADS):
-        if cfgs is not None and cfg not in cfgs:
-            continue
-        inp = W.make_inputs(cfg, wl, threads=workers)
-        _ORACLE_INPUTS.clear()
-        _ORACLE_INPUTS[cfg] = (wl, inp)
-        whole = cfg < 3
-        rows = np.arange(wl.n_tokens) if whole else oracle_rows(wl, subset_random)
-        # head-major order: consecutive units of one worker share a head
-        units = [(cfg, h, rows[i:i + block]) for h in range(wl.heads) for i in range(0, len(rows), block)]
-        print(f"[oracle] {wl.name}: {len(rows)} rows x {wl.heads} heads, {len(units)} units", file=sys.stderr,
-              flush=True)
-        t0 = time.perf_counter()
-        with mp.get_context("fork").Pool(workers) as pool:
-            busy = sum(pool.map(_oracle_unit, units, chunksize=1))
-        wall = time.perf_counter() - t0
-        frac = len(rows) / wl.n_tokens
-        res["workloads"].append({
-            "workload": wl.name, "n_tokens": wl.n_tokens, "heads": wl.heads, "rows": int(len(rows)),
-            "whole": whole, "wall_s": round(wall, 1), "worker_busy_s": round(busy, 1),
-            "full_wall_s" if whole else "full_wall_s_extrapolated": round(wall / frac, 1)})
-        print(json.dumps(res["workloads"][-1]), file=sys.stderr, flush=True)
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers) as pool:
+        for cfg, wl in enumerate(W.WORKLOADS):
+            if cfgs is not None and cfg not in cfgs:
+                continue
+            whole = cfg < 3
+            rows = np.arange(wl.n_tokens) if whole else oracle_rows(wl, subset_random)
+            # head-major order: consecutive units of one worker share a head
+            units = [(cfg, h, rows[i:i + block]) for h in range(wl.heads) for i in range(0, len(rows), block)]
+            print(f"[oracle] {wl.name}: {len(rows)} rows x {wl.heads} heads, {len(units)} units", file=sys.stderr,
+                  flush=True)
+            t0 = time.perf_counter()
+            prep, attn, preps, done, step = 0.0, 0.0, 0, 0, max(1, len(units) // 20)
+            for dp, da, fresh in pool.imap(_oracle_unit, units, chunksize=1):
+                prep += dp
+                attn += da
+                preps += fresh
+                done += 1
+                if done % step == 0:
+                    print(f"[oracle] {wl.name}: {done}/{len(units)} units, {time.perf_counter() - t0:.0f} s",
+                          file=sys.stderr, flush=True)
+            wall = time.perf_counter() - t0
+            entry = {"workload": wl.name, "n_tokens": wl.n_tokens, "heads": wl.heads, "rows": int(len(rows)),
+                     "whole": whole, "wall_s": round(wall, 1), "worker_busy_s": round(prep + attn, 1),
+                     "prep_busy_s": round(prep, 1), "head_preps": int(preps)}
+            if whole:
+                entry["full_wall_s"] = round(wall, 1)
+            else:
+                # a whole run: every worker prepares each head once (units of a head
+                # outnumber the workers), the attention grows with the rows
+                full_busy = workers * wl.heads * prep / max(preps, 1) + attn * wl.n_tokens / len(rows)
+                entry["full_wall_s_extrapolated"] = round(full_busy / workers, 1)
+            res["workloads"].append(entry)
+            print(json.dumps(res["workloads"][-1]), file=sys.stderr, flush=True)
     print(json.dumps(res), flush=True)
 
 

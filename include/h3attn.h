@@ -22,8 +22,9 @@
  * - The caller owns every buffer.  The library never allocates, never frees,
  *   never synchronises and keeps no state between calls; calls on different
  *   streams may run concurrently.  `stream` is a hipStream_t (NULL = the
- *   default stream).  Work is enqueued on `stream`; results are ready when the
- *   stream reaches that point.
+ *   default stream), passed as void* so that this header needs no HIP header
+ *   and the library can be called from plain C.  Work is enqueued on `stream`;
+ *   results are ready when the stream reaches that point.
  * - Strides are in ELEMENTS of the tensor's type, the last (head-dim) axis is
  *   contiguous.  Q/K/V inputs are strided NHD views, e.g. slices of an
  *   interleaved QKV projection output ("H3 Runtime Current State", Owned
@@ -70,7 +71,13 @@ typedef struct {
     int32_t head_dim;           /* d: must be 128                                       */
     int32_t rope_sections[3];   /* widths of the t, h, w slices of d, in this order:
                                    contiguous [0,s0), [s0,s0+s1), [s0+s1,d); each >= 0,
-                                   a multiple of 16, summing to d (e.g. 32, 48, 48)    */
+                                   a multiple of 16, summing to d (e.g. 32, 48, 48).
+                                   Split-half RoPE pairs element j of a section's first
+                                   half with j of its second half; the kernels give each
+                                   lane an 8-element chunk of a first half and its
+                                   partner chunk, so halves must be whole chunks: an
+                                   even width that is not a multiple of 16 returns
+                                   H3ATTN_E_UNSUPPORTED (no cross-lane pairing is built) */
     float rope_theta;           /* RoPE base, > 0 (e.g. 10000)                          */
     float rms_eps;              /* RMSNorm epsilon, >= 0 (e.g. 1e-6)                    */
     int32_t qk_format;          /* h3attn_qk_format                                     */

@@ -62,7 +62,10 @@ def test_oracle_subset_whole_tiny_workload_and_extrapolation():
     wl = W.ragged_workload(5000, 3)
     r = bench.oracle_subset(wl, W.make_inputs(7, wl), 32, heads_n=1)
     assert r["full_s"] is None and r["heads"] == 1
-    assert r["full_s_extrapolated"] == pytest.approx(r["seconds"] * 5000 * 3 / r["rows"], rel=0.01)
+    # the per-head prep of all keys counts once per head, the attention per row
+    rows_s = r["seconds"] - r["prep_s"]
+    expect = 3 * (r["prep_s"] + rows_s * 5000 / r["rows"])
+    assert r["full_s_extrapolated"] == pytest.approx(expect, rel=0.01, abs=0.1)
 
 
 def test_full_oracle_mode_on_the_tiny_workload(capsys):
@@ -72,6 +75,8 @@ def test_full_oracle_mode_on_the_tiny_workload(capsys):
     out = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
     assert out["workloads"][0]["whole"] and out["workloads"][0]["rows"] == W.WORKLOADS[0].n_tokens
     assert out["workers"] >= 1 and "cpu_count" in out["host"]
+    # 4 heads x 2 row blocks: every head prepared at least once, at most once per unit
+    assert 4 <= out["workloads"][0]["head_preps"] <= 8
 
 
 def test_clock_sampler_reads_the_starred_level(tmp_path):
