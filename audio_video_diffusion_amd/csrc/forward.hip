@@ -139,9 +139,16 @@ __device__ __forceinline__ void dma16_buf(const u32x4& rsrc, uint32_t voff, uint
 // stays in AGPRs: these MFMAs are issued as inline asm to pin the register
 // classes.  The first of a chain writes an early-clobber destination (it must
 // not overlap the A/B operands); the rest accumulate in place.
+// A matrix-core product reads a VGPR two wait states after a VALU write of it
+// at the earliest (the compiler pads its own products so on gfx950), but it
+// cannot see a product inside asm: the chain's first product, whose operands
+// (the start value above all) the compiler may materialise with VALU moves
+// just before it, therefore starts with s_nop 1.  The later products of a
+// chain read the previous product's result (forwarded) and operands loaded
+// from LDS.
 __device__ __forceinline__ void mfma_s(f32x16& d, const bf16x8& a, const bf16x8& b, bool first) {
     if (first)
-        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
     else
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
@@ -149,7 +156,7 @@ __device__ __forceinline__ void mfma_s(f32x16& d, const bf16x8& a, const bf16x8&
 // The chain's first product of the fused-Q form: it adds to c0, which holds
 // -m in every element (the running max leaves with the start value).
 __device__ __forceinline__ void mfma_s_from(f32x16& d, const bf16x8& a, const bf16x8& b, const f32x16& c0) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c0));
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c0));
 }
 
 // The int8 form of mfma_s: int32 scores in arch VGPRs (the softmax converts
@@ -159,7 +166,7 @@ __device__ __forceinline__ void mfma_s_from(f32x16& d, const bf16x8& a, const bf
 __device__ __forceinline__ void mfma_s_i8(i32x16& d, const i32x4& a, const i32x4& b, bool first,
                                           const i32x16& c0) {
     if (first)
-        asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c0));
+        asm("s_nop 1\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c0));
     else
         asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }

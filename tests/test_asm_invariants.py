@@ -15,7 +15,14 @@ protocols need:
   them vmcnt(0) (which would drain the prefetch);
 * every VALU read of a result of an inline-asm matrix-core product comes at
   least 19 wait states after that product (the gfx950 XDL-write -> VALU-read
-  spacing for a 16-pass product, with one to spare over the 8-pass forms).
+  spacing for a 16-pass product, with one to spare over the 8-pass forms);
+* every inline-asm matrix-core product comes at least 2 wait states after the
+  last VALU write of any of its source registers (A, B or C; the gfx950
+  VALU-write -> XDL-read spacing, which the compiler enforces for its own
+  products only);
+* no transposing LDS read (ds_read_b64_tr_b16) writes accumulation registers:
+  every form that is checked against the oracle takes them into VGPRs, and a
+  build that took some into AGPRs computed wrong rows, for a reason not found.
 """
 import re
 import shutil
@@ -38,6 +45,7 @@ KERNELS = {
     "ILb1ELb1ELb0ELi4ELb1E": "int32 scores hook, four waves",
 }
 MFMA_VALU_WAIT_STATES = 19
+VALU_MFMA_WAIT_STATES = 2
 
 
 @pytest.fixture(scope="module")
@@ -193,3 +201,35 @@ def test_mfma_results_read_after_wait_states(kernels, key):
             ws += wait_states(t)
     if "scores" not in KERNELS[key]:
         assert checked > 0, KERNELS[key]
+
+
+@pytest.mark.parametrize("key", sorted(KERNELS))
+def test_mfma_sources_written_before_wait_states(kernels, key):
+    ins = instructions(kernels[key][0])
+    products = 0
+    for i, s, in_asm in ins:
+        if not (in_asm and s.startswith("v_mfma")):
+            continue
+        products += 1
+        _, ops = operands(s)
+        src = set().union(*[regs(o) for o in ops[1:]])
+        ws = 0
+        for j in range(i - 1, max(-1, i - 16), -1):
+            t = ins[j][1]
+            top, tops = operands(t)
+            if top.startswith("s_cbranch") or top.startswith("s_branch"):
+                break
+            if top.startswith("v_") and not top.startswith("v_mfma") and tops and regs(tops[0]) & src:
+                assert ws >= VALU_MFMA_WAIT_STATES, (KERNELS[key], t, s, ws)
+                break
+            ws += wait_states(t)
+    assert products > 0, KERNELS[key]
+
+
+@pytest.mark.parametrize("key", sorted(KERNELS))
+def test_transposing_lds_reads_land_in_vgprs(kernels, key):
+    ins = instructions(kernels[key][0])
+    tr = [s for _, s, _ in ins if s.startswith("ds_read_b64_tr")]
+    for s in tr:
+        _, ops = operands(s)
+        assert ops[0].startswith("v"), (KERNELS[key], s)
