@@ -409,6 +409,15 @@ fwd8_kernel(FwdParams P) {
     i32x16 bias16;
 #pragma unroll
     for (int e = 0; e < 16; ++e) bias16[e] = kI8BiasBits;
+    // A matrix-core product reads its C operand late, while the wave issues
+    // on: a write to those registers within a few wait states of the product
+    // (up to 15 for a 32x32 product) can reach it first.  The compiler cannot
+    // see that for a product in asm; it would rebuild the chain-start values
+    // (bias16 here, negm in the fused form) before each chain and hand their
+    // registers to other values right after it.  Made opaque here and used
+    // again after the tile loop, they stay in registers, untouched by anything
+    // but their own updates, for the whole loop.
+    asm volatile("" : "+v"(bias16));
     if constexpr (kInt8 && !kScores) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
     // K block scales through the constant address space: one scalar load per
     // tile, counted by lgkmcnt.  A vector load would be waited for with
@@ -431,6 +440,7 @@ fwd8_kernel(FwdParams P) {
     // mch is the running max except before the first tile (m = -inf, mch = 0).
     float mch = 0.f;
     f32x16 negm = f32x16{};
+    if constexpr (kFuseQ) asm volatile("" : "+v"(negm));     // see bias16
 
     const int ntiles = (n + kBN - 1) / kBN;
     // key tiles jb..last run (the scores hook: the tiles of its key window)
@@ -686,6 +696,7 @@ fwd8_kernel(FwdParams P) {
                             mch = m;
 #pragma unroll
                             for (int e = 0; e < 16; ++e) negm[e] = -m;
+                            asm volatile("" : "+v"(negm));
                         }
                     }
                 l += t;
@@ -763,6 +774,9 @@ fwd8_kernel(FwdParams P) {
     __syncthreads();
     for (int j = jb; j < last; ++j) tile(j, false);
     tile(last, ragged);
+    // the chain-start values stay allocated until every chain has read them
+    if constexpr (kInt8) asm volatile("" ::"v"(bias16));
+    if constexpr (kFuseQ) asm volatile("" ::"v"(negm));
     wait_vmem_all();
     if constexpr (kScores) return;
     // O is complete here in every lane.  A matrix-core product reads the

@@ -16,13 +16,18 @@ protocols need:
 * every VALU read of a result of an inline-asm matrix-core product comes at
   least 19 wait states after that product (the gfx950 XDL-write -> VALU-read
   spacing for a 16-pass product, with one to spare over the 8-pass forms);
-* every inline-asm matrix-core product comes at least 2 wait states after the
-  last VALU write of any of its source registers (A, B or C; the gfx950
-  VALU-write -> XDL-read spacing, which the compiler enforces for its own
-  products only);
-* no transposing LDS read (ds_read_b64_tr_b16) writes accumulation registers:
-  every form that is checked against the oracle takes them into VGPRs, and a
-  build that took some into AGPRs computed wrong rows, for a reason not found.
+* every matrix-core product comes at least 2 wait states after the last VALU
+  write of any of its source registers (A, B or C; the gfx950 VALU-write ->
+  XDL-read spacing, which the compiler enforces only for writes it can see,
+  not for the products or the accumulator writes the kernel issues in asm);
+* nothing writes the C-operand registers of an inline-asm product whose C is
+  not its own destination (a chain's first product) within 18 wait states of
+  it: a product reads C late, and a 32x32 product needs at most 15 (the
+  compiler, blind to the asm product, once handed those registers to a VALU
+  result 0-3 wait states later in a stage-unrolled build of the loop, which
+  then computed wrong rows);
+* no transposing LDS read (ds_read_b64_tr_b16) writes accumulation registers
+  (every form checked against the oracle takes them into VGPRs).
 """
 import re
 import shutil
@@ -46,6 +51,7 @@ KERNELS = {
 }
 MFMA_VALU_WAIT_STATES = 19
 VALU_MFMA_WAIT_STATES = 2
+SRCC_WAR_WAIT_STATES = 18
 
 
 @pytest.fixture(scope="module")
@@ -208,7 +214,7 @@ def test_mfma_sources_written_before_wait_states(kernels, key):
     ins = instructions(kernels[key][0])
     products = 0
     for i, s, in_asm in ins:
-        if not (in_asm and s.startswith("v_mfma")):
+        if not s.startswith("v_mfma"):
             continue
         products += 1
         _, ops = operands(s)
@@ -233,3 +239,31 @@ def test_transposing_lds_reads_land_in_vgprs(kernels, key):
     for s in tr:
         _, ops = operands(s)
         assert ops[0].startswith("v"), (KERNELS[key], s)
+
+
+WRITERS = ("v_", "ds_read", "buffer_load", "global_load", "scratch_load", "flat_load")
+
+
+@pytest.mark.parametrize("key", sorted(KERNELS))
+def test_chain_start_c_operand_not_overwritten_early(kernels, key):
+    ins = instructions(kernels[key][0])
+    starts = 0
+    for i, s, in_asm in ins:
+        if not (in_asm and s.startswith("v_mfma")):
+            continue
+        _, ops = operands(s)
+        c, d = regs(ops[3]), regs(ops[0])
+        if not c or c == d:
+            continue
+        starts += 1
+        ws = 0
+        for j in range(i + 1, min(len(ins), i + 80)):
+            t = ins[j][1]
+            top, tops = operands(t)
+            if top.startswith(("s_cbranch", "s_branch", "s_endpgm")) or ws >= SRCC_WAR_WAIT_STATES:
+                break
+            if tops and top.startswith(WRITERS) and regs(tops[0]) & c:
+                assert False, (KERNELS[key], s, t, ws)
+            ws += wait_states(t)
+    if "int8" in KERNELS[key] or "fused" in KERNELS[key] or "scores" in KERNELS[key]:
+        assert starts > 0, KERNELS[key]
