@@ -60,11 +60,11 @@ PEAK_HBM_GBS = 8000.0
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
     "kernel": "h3attn_forward_fused_q",
-    "source_sha256": "66aec44030ef15f2983bf2a2fff1ce3aeef036a94ad84d5ffd54d54fbdd9556a",
+    "source_sha256": "3dad80699bea3c3e56c5c29c5276424eb50bfff1dcb2493abf87b02abee58719",
     # the copy's kernel reads 524,319 KiB per 1 GiB as FETCH_SIZE (factor 2.0) and
     # writes 1,048,576 KiB as WRITE_SIZE (factor 1.0)
-    "fetch_kib": 68524297.0, "fetch_scale": 2.0,
-    "write_kib": 776660.0, "write_scale": 1.0,
+    "fetch_kib": 13350841.9, "fetch_scale": 2.0,
+    "write_kib": 821883.2, "write_scale": 1.0,
 }
 
 
