@@ -129,12 +129,12 @@ int prep_common(const h3attn_problem* p,
                 const void* gamma_q, const void* gamma_k, int64_t gamma_head_stride,
                 const int32_t* pos_thw,
                 void* q_out, void* k_out, float* q_scales, float* k_scales,
-                float* k_mean, bool smooth, bool k_only, void* stream) {
+                float* k_mean, bool smooth, bool k_only, bool k_only_i8, void* stream) {
     int rc = check_problem(p);
     if (rc) return rc;
     const bool i8 = p->qk_format == H3ATTN_QK_I8_BLK64;
     if (smooth && !i8) return H3ATTN_E_UNSUPPORTED;
-    if (k_only && i8) return H3ATTN_E_UNSUPPORTED;
+    if (k_only && i8 != k_only_i8) return H3ATTN_E_UNSUPPORTED;
     if (smooth && !k_mean) return H3ATTN_E_NULL;
     if (smooth && !aligned(k_mean, 4)) return H3ATTN_E_ALIGN;
     if (k_only) {
@@ -142,6 +142,7 @@ int prep_common(const h3attn_problem* p,
         q = k; q_stride_tok = k_stride_tok; q_stride_head = k_stride_head;
         gamma_q = gamma_k;
         q_out = k_out;
+        q_scales = k_scales;
     }
     if ((rc = check_in_view(q, q_stride_tok, q_stride_head))) return rc;
     if ((rc = check_in_view(k, k_stride_tok, k_stride_head))) return rc;
@@ -162,13 +163,14 @@ int prep_common(const h3attn_problem* p,
                           span(pos_thw, (size_t)n * 3 * sizeof(int32_t))};
     Range outs[5] = {span(q_out, out_b), span(k_out, out_b), {0, 0}, {0, 0}, {0, 0}};
     int nout = smooth ? 5 : i8 ? 4 : 2;
-    if (k_only) {
-        outs[0] = outs[1];
-        nout = 1;
-    }
     if (i8) {
         outs[2] = span(q_scales, sc_b);
         outs[3] = span(k_scales, sc_b);
+    }
+    if (k_only) {                // K' (and its scales) only
+        outs[0] = outs[1];
+        outs[1] = outs[3];
+        nout = i8 ? 2 : 1;
     }
     if (smooth) outs[4] = span(k_mean, (size_t)h * 128 * sizeof(float));
     for (int o = 0; o < nout; ++o) {
@@ -191,10 +193,10 @@ int prep_common(const h3attn_problem* p,
     P.sec0 = p->rope_sections[0]; P.sec1 = p->rope_sections[1]; P.sec2 = p->rope_sections[2];
     P.k_mean = k_mean;
     if (k_only) {
-        P.q = nullptr; P.gq = nullptr; P.q_out = nullptr;
+        P.q = nullptr; P.gq = nullptr; P.q_out = nullptr; P.q_scales = nullptr;
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipError_t e = smooth ? h3::launch_prep_ksmooth(P, st) : k_only ? h3::launch_prep_k(P, st)
+    const hipError_t e = smooth ? h3::launch_prep_ksmooth(P, st) : k_only ? h3::launch_prep_k(P, i8, st)
                                                                           : h3::launch_prep(P, i8, st);
     if (e != hipSuccess) return H3ATTN_E_HIP;
     return H3ATTN_OK;
@@ -212,14 +214,22 @@ int h3attn_prep(const h3attn_problem* p,
                 void* q_out, void* k_out, float* q_scales, float* k_scales,
                 void* stream) {
     return prep_common(p, q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, gamma_q, gamma_k,
-                       gamma_head_stride, pos_thw, q_out, k_out, q_scales, k_scales, nullptr, false, false, stream);
+                       gamma_head_stride, pos_thw, q_out, k_out, q_scales, k_scales, nullptr, false, false, false,
+                       stream);
 }
 
 int h3attn_prep_k(const h3attn_problem* p, const void* k, int64_t k_stride_tok, int64_t k_stride_head,
                   const void* gamma_k, int64_t gamma_head_stride, const int32_t* pos_thw, void* k_out,
                   void* stream) {
     return prep_common(p, nullptr, 0, 0, k, k_stride_tok, k_stride_head, nullptr, gamma_k, gamma_head_stride,
-                       pos_thw, nullptr, k_out, nullptr, nullptr, nullptr, false, true, stream);
+                       pos_thw, nullptr, k_out, nullptr, nullptr, nullptr, false, true, false, stream);
+}
+
+int h3attn_prep_k_i8(const h3attn_problem* p, const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                     const void* gamma_k, int64_t gamma_head_stride, const int32_t* pos_thw, void* k_out,
+                     float* k_scales, void* stream) {
+    return prep_common(p, nullptr, 0, 0, k, k_stride_tok, k_stride_head, nullptr, gamma_k, gamma_head_stride,
+                       pos_thw, nullptr, k_out, nullptr, k_scales, nullptr, false, true, true, stream);
 }
 
 int h3attn_prep_ksmooth(const h3attn_problem* p,
@@ -230,20 +240,22 @@ int h3attn_prep_ksmooth(const h3attn_problem* p,
                         void* q_out, void* k_out, float* q_scales, float* k_scales,
                         float* k_mean, void* stream) {
     return prep_common(p, q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, gamma_q, gamma_k,
-                       gamma_head_stride, pos_thw, q_out, k_out, q_scales, k_scales, k_mean, true, false, stream);
+                       gamma_head_stride, pos_thw, q_out, k_out, q_scales, k_scales, k_mean, true, false, false,
+                       stream);
 }
 
 }  // extern "C"
 
 namespace {
 
-// Raw-Q inputs of h3attn_forward_fused_q.
+// Raw-Q inputs of h3attn_forward_fused_q and h3attn_forward_fused_q_i8.
 struct RawQ {
     const void* q;
     int64_t st, sh;
     const void* gamma;
     int64_t g_sh;
     const int32_t* pos;
+    bool int8;           // the entry point's format
 };
 
 // Shared by h3attn_forward (bf16 V view), h3attn_forward_fp8v (staged E4M3 V)
@@ -257,12 +269,13 @@ int forward_common(const h3attn_problem* p, const void* q_prep, const void* k_pr
     if (rc) return rc;
     const bool i8 = p->qk_format == H3ATTN_QK_I8_BLK64;
     if (rq) {
-        if (i8 || fp8v) return H3ATTN_E_UNSUPPORTED;
+        if (i8 != rq->int8 || fp8v) return H3ATTN_E_UNSUPPORTED;
         if ((rc = check_in_view(rq->q, rq->st, rq->sh))) return rc;
         if ((rc = check_in_view(rq->gamma, 0, rq->g_sh))) return rc;
         if (!rq->pos) return H3ATTN_E_NULL;
         if (!aligned(rq->pos, 4)) return H3ATTN_E_ALIGN;
-        q_prep = k_prep;     // placeholder for the checks below; never read
+        q_prep = k_prep;     // placeholders for the checks below; never read
+        if (i8) q_scales = k_scales;
     }
     if (!q_prep || !k_prep) return H3ATTN_E_NULL;
     if (!aligned(q_prep, 16) || !aligned(k_prep, 16)) return H3ATTN_E_ALIGN;
@@ -315,13 +328,14 @@ int forward_common(const h3attn_problem* p, const void* q_prep, const void* k_pr
     P.c = (float)((double)softmax_scale * 1.4426950408889634);
     if (rq) {
         P.q = nullptr;
+        P.qs = nullptr;
         P.qraw = static_cast<const uint16_t*>(rq->q); P.q_st = rq->st; P.q_sh = rq->sh;
         P.gq = static_cast<const uint16_t*>(rq->gamma); P.g_sh = rq->g_sh;
         P.pos = rq->pos;
         P.eps = p->rms_eps;
         P.rho0 = rope_ratio(p, 0); P.rho1 = rope_ratio(p, 1); P.rho2 = rope_ratio(p, 2);
         P.sec0 = p->rope_sections[0]; P.sec1 = p->rope_sections[1]; P.sec2 = p->rope_sections[2];
-        if (h3::launch_forward_fused_q(P, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
+        if (h3::launch_forward_fused_q(P, i8, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
         return H3ATTN_OK;
     }
     if (h3::launch_forward(P, i8, fp8v, static_cast<hipStream_t>(stream)) != hipSuccess) return H3ATTN_E_HIP;
@@ -349,8 +363,20 @@ int h3attn_forward_fused_q(const h3attn_problem* p,
                            const void* v, int64_t v_stride_tok, int64_t v_stride_head,
                            void* o, int64_t o_stride_tok, int64_t o_stride_head,
                            float softmax_scale, void* stream) {
-    const RawQ rq{q, q_stride_tok, q_stride_head, gamma_q, gamma_head_stride, pos_thw};
+    const RawQ rq{q, q_stride_tok, q_stride_head, gamma_q, gamma_head_stride, pos_thw, false};
     return forward_common(p, nullptr, k_prep, nullptr, nullptr, false, v, v_stride_tok, v_stride_head, nullptr,
+                          o, o_stride_tok, o_stride_head, softmax_scale, &rq, stream);
+}
+
+int h3attn_forward_fused_q_i8(const h3attn_problem* p,
+                              const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                              const void* gamma_q, int64_t gamma_head_stride, const int32_t* pos_thw,
+                              const void* k_codes, const float* k_scales,
+                              const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                              void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                              float softmax_scale, void* stream) {
+    const RawQ rq{q, q_stride_tok, q_stride_head, gamma_q, gamma_head_stride, pos_thw, true};
+    return forward_common(p, nullptr, k_codes, nullptr, k_scales, false, v, v_stride_tok, v_stride_head, nullptr,
                           o, o_stride_tok, o_stride_head, softmax_scale, &rq, stream);
 }
 

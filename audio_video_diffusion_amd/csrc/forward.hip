@@ -302,10 +302,12 @@ constexpr int32_t kI8BiasBits = 0x4b400000;
 // factor multiplies numerator and denominator alike and cancels.
 constexpr float kPLog2Fp8 = 0.8f;
 
-// kFuseQ (bf16 only): Q' is not read from memory but computed in the prologue
-// from raw Q with the prep kernel's own per-row routine (rope_norm.h), rounded
-// to bf16 once with the base-2 logit factor folded in; each Q'K'^T chain then
-// starts from -m, so the scores leave the matrix core ready for exp2.
+// kFuseQ: Q' is not read from memory but computed in the prologue from raw Q
+// with the prep kernel's own per-row routine (rope_norm.h).  bf16 format
+// (kFuseBf): rounded to bf16 once with the base-2 logit factor folded in; each
+// Q'K'^T chain then starts from -m, so the scores leave the matrix core ready
+// for exp2.  Int8 format: rounded to bf16 and quantised per 64-row block
+// exactly as the prep does (codes and scales identical), then the int8 path.
 // kW = 4 (int8 K' with E4M3 V only): four waves own 128 query rows and the
 // stages take 64 KB of LDS, so two independent work-groups share each CU (one
 // wave of each per SIMD).  Their barriers are unrelated, so the two waves of a
@@ -321,7 +323,10 @@ constexpr float kPLog2Fp8 = 0.8f;
 template <bool kInt8, bool kFp8V, bool kFuseQ = false, int kW = 8, bool kScores = false>
 __global__ void __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd8_kernel(FwdParams P) {
-    static_assert(!(kFuseQ && kInt8), "the fused Q prologue produces bf16 Q'");
+    static_assert(!(kFuseQ && (kFp8V || kScores || kW != 8)), "the fused Q prologue: bf16 V, eight waves");
+    // fused Q in the bf16 format: Q' carries the logit scale and the chains start
+    // from -m (the int8 form quantises Q' as the prep does and runs the int8 path)
+    constexpr bool kFuseBf = kFuseQ && !kInt8;
     static_assert(kW == 8 || (kW == 4 && kInt8 && kFp8V), "four waves: int8 K' with E4M3 V only");
     static_assert(!kScores || kInt8, "the scores hook covers the int8 Q'K'^T path");
     constexpr int kBMw = 32 * kW;                  // query rows per work-group
@@ -423,7 +428,7 @@ fwd8_kernel(FwdParams P) {
     // again after the tile loop, they stay in registers, untouched by anything
     // but their own updates, for the whole loop.
     asm volatile("" : "+v"(bias16));
-    if constexpr (kInt8 && !kScores) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
+    if constexpr (kInt8 && !kScores && !kFuseQ) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
     // K block scales through the constant address space: one scalar load per
     // tile, counted by lgkmcnt.  A vector load would be waited for with
     // vmcnt(0), which also drains the buffer -> LDS prefetch.
@@ -440,12 +445,12 @@ fwd8_kernel(FwdParams P) {
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) O[cc] = f32x16{};
     float m = -INFINITY, l = 0.f;
-    // kFuseQ: Q' carries the base-2 logit scale, and every Q'K'^T chain starts
+    // kFuseBf: Q' carries the base-2 logit scale, and every Q'K'^T chain starts
     // from -mch (negm), so the scores come out as logit - mch, ready for exp2.
     // mch is the running max except before the first tile (m = -inf, mch = 0).
     float mch = 0.f;
     f32x16 negm = f32x16{};
-    if constexpr (kFuseQ) asm volatile("" : "+v"(negm));     // see bias16
+    if constexpr (kFuseBf) asm volatile("" : "+v"(negm));     // see bias16
 
     const int ntiles = (n + kBN - 1) / kBN;
     // key tiles jb..last run (the scores hook: the tiles of its key window)
@@ -532,7 +537,7 @@ fwd8_kernel(FwdParams P) {
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-                if (kFuseQ && t == 0) {
+                if (kFuseBf && t == 0) {
                     mfma_s_from(S[0], a[0][t], q[t], negm);
                     mfma_s_from(S[1], a[1][t], q[t], negm);
                 } else {
@@ -587,7 +592,7 @@ fwd8_kernel(FwdParams P) {
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) mx = __builtin_fmaxf(mx, S[kb][e]);
-                mx = kInt8 ? (max_halves(mx) - kI8Bias) * coef : kFuseQ ? max_halves(mx) + mch : max_halves(mx) * coef;
+                mx = kInt8 ? (max_halves(mx) - kI8Bias) * coef : kFuseBf ? max_halves(mx) + mch : max_halves(mx) * coef;
                 if (__any(mx > m + kRescaleLog2)) {
                     const float mm = fmaxf(m, mx);
                     const float alpha = __builtin_amdgcn_exp2f(m - mm);
@@ -655,7 +660,7 @@ fwd8_kernel(FwdParams P) {
             } else {
                 bf16x8 Pb[2][2];
                 float rs[2];
-                // shifted (kFuseQ, after m was raised): the scores still hold
+                // shifted (kFuseBf, after m was raised): the scores still hold
                 // logit - mch, so m - mch more is subtracted
                 auto make_p = [&](const bool shifted) {
                     // int8: the score bias leaves with the max (kI8Bias)
@@ -671,7 +676,7 @@ fwd8_kernel(FwdParams P) {
                             for (int ii = 0; ii < 4; ++ii) {
                                 const int e = 8 * s + 2 * ii;
                                 float x0, x1;
-                                if constexpr (kFuseQ) {
+                                if constexpr (kFuseBf) {
                                     x0 = __builtin_amdgcn_exp2f(shifted ? S[kb][e] + off : S[kb][e]);
                                     x1 = __builtin_amdgcn_exp2f(shifted ? S[kb][e + 1] + off : S[kb][e + 1]);
                                 } else {
@@ -692,12 +697,12 @@ fwd8_kernel(FwdParams P) {
                 };
                 make_p(false);
                 float t = rs[0] + rs[1];
-                // kFuseQ: the first tile sets the running max (its chain started from 0)
-                if (masked || (kFuseQ && j == 0) || __any(!(t <= kSumCheck)))
+                // kFuseBf: the first tile sets the running max (its chain started from 0)
+                if (masked || (kFuseBf && j == 0) || __any(!(t <= kSumCheck)))
                     if (raise_max()) {
                         make_p(true);
                         t = rs[0] + rs[1];
-                        if constexpr (kFuseQ) {
+                        if constexpr (kFuseBf) {
                             mch = m;
 #pragma unroll
                             for (int e = 0; e < 16; ++e) negm[e] = -m;
@@ -735,7 +740,7 @@ fwd8_kernel(FwdParams P) {
     fetch(jb);
     fetch(jb + 1);
     if constexpr (kAhead == 3) fetch(jb + 2);
-    if constexpr (kFuseQ) {
+    if constexpr (kFuseBf) {
         // Q' of the work-group's 256 rows, computed while tiles 0..2 stream
         // in, in two halves of 128 rows staged through LDS stage 3 (K' part:
         // rows 0..63 of the half, V part: rows 64..127), 16-byte chunks
@@ -775,6 +780,77 @@ fwd8_kernel(FwdParams P) {
             __syncthreads();
         }
     }
+    if constexpr (kFuseQ && kInt8) {
+        // Int8 Q': the work-group's 256 rows are four 64-row quantisation
+        // blocks; thread (r = tid / 8, slot tid % 8) prepares row r of each.
+        // Per half (blocks 2h, 2h + 1): Q' rounded to bf16 exactly as the prep
+        // does, the block absmax over the work-group, the prep's scale and
+        // codes, staged through V stage 3 (128 int8 rows, 16-byte chunks
+        // XOR-swizzled as the K' tiles); waves 4h..4h+3 take their operands and
+        // their block's scale from half h.
+        float ga[8], gb[8];
+        unpack8(fga, ga);
+        unpack8(fgb, gb);
+        const int r = tid >> 3;
+        float* red = reinterpret_cast<float*>(kbuf(3));          // [8 waves][2 blocks]
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            float rv[2][16];
+            float mx[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int ps = 2 * half + s;
+                float cs[8], sn[8], xa[8], xb[8];
+                rope_angles(fpv[ps], ffreq, cs, sn);
+                unpack8(fqa[ps], xa);
+                unpack8(fqb[ps], xb);
+                u32x4 oa, ob;
+                norm_rotate(xa, xb, ga, gb, cs, sn, P.eps, oa, ob, rv[s], rv[s] + 8);
+                mx[s] = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (qt * kBM + 64 * ps + r >= n) rv[s][i] = 0.f;
+                    mx[s] = fmaxf(mx[s], fabsf(rv[s][i]));
+                }
+#pragma unroll
+                for (int sh = 1; sh < 64; sh <<= 1) mx[s] = fmaxf(mx[s], __shfl_xor(mx[s], sh));
+            }
+            if (lane == 0) {
+                red[2 * wave] = mx[0];
+                red[2 * wave + 1] = mx[1];
+            }
+            __syncthreads();
+            float inv[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                float a = red[s];
+#pragma unroll
+                for (int w = 1; w < 8; ++w) a = fmaxf(a, red[2 * w + s]);
+                // IEEE fp32 divisions, as in the prep (no fast-math in this library)
+                if ((wave >> 2) == half && ((wave >> 1) & 1) == s) qscale = a / 127.0f;
+                inv[s] = a > 0.f ? 127.0f / a : 0.f;
+                const int row = 64 * s + r;                        // row of the half
+                uint8_t* st = vbuf(3) + row * 128;
+                const int sw = k_swizzle<true>(row);
+                const Slot& sl = fsl;
+                *reinterpret_cast<u32x2*>(st + (((sl.a >> 1) ^ sw) * 16) + (sl.a & 1) * 8) =
+                    u32x2{quant4(rv[s], inv[s]), quant4(rv[s] + 4, inv[s])};
+                *reinterpret_cast<u32x2*>(st + (((sl.b >> 1) ^ sw) * 16) + (sl.b & 1) * 8) =
+                    u32x2{quant4(rv[s] + 8, inv[s]), quant4(rv[s] + 12, inv[s])};
+            }
+            __syncthreads();
+            if ((wave >> 2) == half) {
+                const int row = (wave & 3) * 32 + n32;            // row of the half
+                const uint8_t* src = vbuf(3) + row * 128;
+#pragma unroll
+                for (int t = 0; t < kSteps; ++t)
+                    q[t] = *reinterpret_cast<const QOp*>(src + (((2 * t + hh) ^ k_swizzle<true>(row)) * 16));
+            }
+            // the staging reads are complete before stage 3 is written again
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+    }
     wait_vmem_upto<(kAhead - 1) * kDma8>();
     __syncthreads();
     // Fused Q and int8 Q'/K' with bf16 V run the loop unrolled by the four
@@ -798,7 +874,7 @@ fwd8_kernel(FwdParams P) {
     tile(last, ragged, last % kStages);
     // the chain-start values stay allocated until every chain has read them
     if constexpr (kInt8) asm volatile("" ::"v"(bias16));
-    if constexpr (kFuseQ) asm volatile("" ::"v"(negm));
+    if constexpr (kFuseBf) asm volatile("" ::"v"(negm));
     wait_vmem_all();
     if constexpr (kScores) return;
     // O is complete here in every lane.  A matrix-core product reads the
@@ -841,9 +917,12 @@ hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t 
     return hipGetLastError();
 }
 
-hipError_t launch_forward_fused_q(const FwdParams& P, hipStream_t stream) {
+hipError_t launch_forward_fused_q(const FwdParams& P, bool int8, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
-    hipLaunchKernelGGL((fwd8_kernel<false, false, true>), dim3(kXcds * P.per_xcd), dim3(512), 0, stream, P);
+    if (int8)
+        hipLaunchKernelGGL((fwd8_kernel<true, false, true>), dim3(P.total), dim3(512), 0, stream, P);
+    else
+        hipLaunchKernelGGL((fwd8_kernel<false, false, true>), dim3(kXcds * P.per_xcd), dim3(512), 0, stream, P);
     return hipGetLastError();
 }
 

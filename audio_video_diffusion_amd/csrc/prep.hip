@@ -29,30 +29,22 @@
 namespace h3 {
 
 
-__device__ __forceinline__ uint32_t quant4(const float* v, float inv) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float c = __builtin_rintf(v[i] * inv);
-        c = fminf(fmaxf(c, -127.f), 127.f);
-        w |= (uint32_t)((int)c & 0xff) << (8 * i);
-    }
-    return w;
-}
 
 // kPrepI8Sums and kPrepI8Smooth are the first and last pass of K smoothing:
 // the first writes Q' codes as kPrepI8 does, and for K' the per-block channel
 // sums of its bf16 values (into the K code buffer, used as scratch); after
 // ksum_reduce has turned them into the channel means, the last recomputes K'
 // alone and quantises fl32(k - mean).
-// kPrepBf16K writes K' alone (for the forward that computes Q' in its prologue).
-enum PrepMode { kPrepBf16 = 0, kPrepI8 = 1, kPrepI8Sums = 2, kPrepI8Smooth = 3, kPrepBf16K = 4 };
+// kPrepBf16K and kPrepI8K write K' alone, bf16 or int8 codes + scales (for the
+// forwards that compute Q' in their prologue).
+enum PrepMode { kPrepBf16 = 0, kPrepI8 = 1, kPrepI8Sums = 2, kPrepI8Smooth = 3, kPrepBf16K = 4, kPrepI8K = 5 };
 
 template <int kMode>
 __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
-    constexpr bool kInt8 = kMode == kPrepI8 || kMode == kPrepI8Sums || kMode == kPrepI8Smooth;
-    constexpr bool kDoQ = kMode != kPrepI8Smooth && kMode != kPrepBf16K;   // Q' produced in this pass
-    constexpr bool kQuantK = kMode == kPrepI8 || kMode == kPrepI8Smooth;
+    constexpr bool kInt8 = kMode == kPrepI8 || kMode == kPrepI8Sums || kMode == kPrepI8Smooth || kMode == kPrepI8K;
+    // Q' produced in this pass
+    constexpr bool kDoQ = kMode != kPrepI8Smooth && kMode != kPrepBf16K && kMode != kPrepI8K;
+    constexpr bool kQuantK = kMode == kPrepI8 || kMode == kPrepI8Smooth || kMode == kPrepI8K;
     const int tid = threadIdx.x;
     const int row = tid >> 3;            // 0..31
     const int p = tid & 7;               // slot
@@ -262,9 +254,12 @@ hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_prep_k(const PrepParams& P, hipStream_t stream) {
+hipError_t launch_prep_k(const PrepParams& P, bool int8, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
-    hipLaunchKernelGGL(prep_kernel<kPrepBf16K>, dim3(P.npad / 64), dim3(256), 0, stream, P);
+    if (int8)
+        hipLaunchKernelGGL(prep_kernel<kPrepI8K>, dim3(P.npad / 64), dim3(256), 0, stream, P);
+    else
+        hipLaunchKernelGGL(prep_kernel<kPrepBf16K>, dim3(P.npad / 64), dim3(256), 0, stream, P);
     return hipGetLastError();
 }
 

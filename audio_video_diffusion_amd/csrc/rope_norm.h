@@ -160,4 +160,20 @@ __device__ __forceinline__ void rope_angles(double pv, const double* f, float* c
     }
 }
 
+// The int8 code of each of v[0..3] at reciprocal scale inv (round to nearest
+// even, clamped to [-127, 127]), packed little-endian: the per-block absmax
+// quantiser of the int8 Q/K path ("H3 Runtime Current State", Owned
+// Performance Kernels: Q quantization, K quantization), shared by the prep and
+// the int8 forward's Q prologue so that both produce the same codes.
+__device__ __forceinline__ uint32_t quant4(const float* v, float inv) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float c = __builtin_rintf(v[i] * inv);
+        c = fminf(fmaxf(c, -127.f), 127.f);
+        w |= (uint32_t)((int)c & 0xff) << (8 * i);
+    }
+    return w;
+}
+
 }  // namespace h3

@@ -27,7 +27,7 @@ SYNC_LIB_PATH = os.path.join(PKG, "libh3attn_sync.so")
 
 QK_BF16 = 0
 QK_I8_BLK64 = 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_UNSUPPORTED", -4: "E_ALIGN",
           -5: "E_ALIAS", -6: "E_HIP"}
@@ -106,6 +106,9 @@ def _load():
         "h3attn_prep_k": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, vp, vp, vp]),
         "h3attn_forward_fused_q": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, vp, vp, vp, i64, i64, vp, i64, i64,
                                                   f32, vp]),
+        "h3attn_prep_k_i8": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, vp, vp, vp, vp]),
+        "h3attn_forward_fused_q_i8": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, vp, vp, vp, vp, i64, i64, vp, i64,
+                                                     i64, f32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -242,6 +245,27 @@ def prep_k(p: Problem, k, gamma_k, pos, k_out, stream=None):
                             _ptr(k_out), _stream(stream))
     if rc:
         raise H3AttnError(rc, "h3attn_prep_k")
+
+
+def prep_k_i8(p: Problem, k, gamma_k, pos, k_out, k_scales, stream=None):
+    """``h3attn_prep_k_i8``: int8 K' codes and block scales alone (int8 problem)."""
+    kp, kst, ksh = _nhd(k, "k")
+    rc = _lib.h3attn_prep_k_i8(ctypes.byref(p), kp, kst, ksh, _ptr(gamma_k), _gamma_stride(gamma_k), _ptr(pos),
+                               _ptr(k_out), _ptr(k_scales), _stream(stream))
+    if rc:
+        raise H3AttnError(rc, "h3attn_prep_k_i8")
+
+
+def forward_fused_q_i8(p: Problem, q, gamma_q, pos, k_codes, k_scales, v, o, softmax_scale: float, stream=None):
+    """``h3attn_forward_fused_q_i8``: the int8 forward from raw Q (q, v, o bf16 [N,H,d] views)."""
+    qp, qst, qsh = _nhd(q, "q")
+    vp, vst, vsh = _nhd(v, "v")
+    op, ost, osh = _nhd(o, "o")
+    rc = _lib.h3attn_forward_fused_q_i8(ctypes.byref(p), qp, qst, qsh, _ptr(gamma_q), _gamma_stride(gamma_q),
+                                        _ptr(pos), _ptr(k_codes), _ptr(k_scales), vp, vst, vsh, op, ost, osh,
+                                        float(softmax_scale), _stream(stream))
+    if rc:
+        raise H3AttnError(rc, "h3attn_forward_fused_q_i8")
 
 
 def forward_fused_q(p: Problem, q, gamma_q, pos, k_prep, v, o, softmax_scale: float, stream=None):

@@ -3,10 +3,11 @@
 
 One step = the whole hot path on one batch of seeded synthetic inputs already
 resident in HBM: Q/K RMSNorm + 3-axis RoPE + head-major layout, then non-causal
-attention over the whole packed sequence.  In the bf16 format the step is
-h3attn_prep_k (K') then h3attn_forward_fused_q (Q' prepared in the forward's
-prologue); with --q-prep separate, or with int8 Q/K or FP8 P V, it is
-h3attn_prep then h3attn_forward (or h3attn_forward_fp8v).
+attention over the whole packed sequence.  With bf16 P V the step is the
+K-only prep then the forward that prepares Q' in its prologue (bf16:
+h3attn_prep_k + h3attn_forward_fused_q; int8 Q/K: h3attn_prep_k_i8 +
+h3attn_forward_fused_q_i8); with --q-prep separate, or with FP8 P V, it is
+h3attn_prep (h3attn_prep_ksmooth) then h3attn_forward (h3attn_forward_fp8v).
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
                     [--qk bf16|int8] [--pv bf16|fp8] [--q-prep fused|separate]
@@ -25,7 +26,8 @@ bounded sample of the headline workload; ``gpu_clock_mhz`` is the shader clock
 sampled during the timed steps.
 
 --forms times each forward form (bf16 Q/K with the Q prep separate or fused,
-int8 Q/K, E4M3 V with bf16 or int8 Q/K) on one workload, one JSON line each:
+int8 Q/K with the Q prep separate or fused, E4M3 V with bf16 or int8 Q/K) on
+one workload, one JSON line each:
 a short program to run under rocprofv3.  --full-oracle runs the CPU oracle
 over every row of the three smaller workloads and over a 2,048-row exact
 subset (plus the sequence ends and modality boundaries, all heads) of the two
@@ -108,8 +110,8 @@ def parse():
     ap.add_argument("--pv", choices=("bf16", "fp8"), default="bf16",
                     help="P V product: bf16, or E4M3 V (staged each step) on the FP8 matrix cores")
     ap.add_argument("--q-prep", choices=("fused", "separate"), default="fused",
-                    help="bf16 Q/K with bf16 P V: Q' prepared in the forward's prologue (default) "
-                         "or by h3attn_prep before h3attn_forward")
+                    help="with bf16 P V: Q' prepared (and in the int8 format quantised) in the forward's "
+                         "prologue (default), or by h3attn_prep before h3attn_forward")
     ap.add_argument("--copy-probe", type=int, default=None, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration) and exit")
     ap.add_argument("--forms", action="store_true",
@@ -370,8 +372,9 @@ def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=No
     With ``vfp8 = (codes, scales)`` each step also stages V as E4M3 (timed on
     its own) and runs the FP8 P V forward; the third list holds those times.
     With ``kmean`` (fp32 [H, 128]) the int8 prep applies K smoothing.
-    With ``fused_q`` (bf16) the prep writes K' alone and the forward prepares
-    Q in its prologue (h3attn_prep_k + h3attn_forward_fused_q).
+    With ``fused_q`` the prep writes K' alone and the forward prepares Q in its
+    prologue (bf16: h3attn_prep_k + h3attn_forward_fused_q; int8:
+    h3attn_prep_k_i8 + h3attn_forward_fused_q_i8).
     """
     import torch
     q, k, v = dev["q"], dev["k"], dev["v"]
@@ -382,7 +385,9 @@ def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=No
     for i in range(warmup + steps):
         e0, e1, e2, e3 = ev(), ev(), ev(), ev()
         e0.record()
-        if fused_q:
+        if fused_q and ks is not None:
+            A.prep_k_i8(p, k, dev["gamma_k"], dev["pos"], k_out, ks)
+        elif fused_q:
             A.prep_k(p, k, dev["gamma_k"], dev["pos"], k_out)
         elif kmean is None:
             A.prep(p, q, k, dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
@@ -392,7 +397,9 @@ def time_step(A, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, heads=No
         if vfp8 is not None:
             A.prep_v_fp8(p, v, vfp8[0], vfp8[1])
         e2.record()
-        if fused_q:
+        if fused_q and ks is not None:
+            A.forward_fused_q_i8(p, q, dev["gamma_q"], dev["pos"], k_out, ks, v, o, scale)
+        elif fused_q:
             A.forward_fused_q(p, q, dev["gamma_q"], dev["pos"], k_out, v, o, scale)
         elif vfp8 is None:
             A.forward(p, q_out, k_out, v, o, scale, qs, ks)
@@ -425,7 +432,7 @@ def sweep(A, W, headline_dev, steps=20, warmup=2, oracle_random=96):
     # bf16 Q/K with bf16 P V: Q prep fused into the forward, as in the timed step
     jobs = [(i, W.WORKLOADS[i], None, W.WORKLOADS[i].qk_int8, False, not W.WORKLOADS[i].qk_int8)
             for i in range(len(W.WORKLOADS)) if i != W.HEADLINE]
-    jobs += [(4, W.WORKLOADS[4], None, True, True, False)]
+    jobs += [(4, W.WORKLOADS[4], None, True, False, True), (4, W.WORKLOADS[4], None, True, True, False)]
     jobs += [(W.HEADLINE, w, w.heads, False, False, True) for w in W.SHARDS]
     jobs += [(W.HEADLINE, hl, hl.heads, False, True, False), (W.HEADLINE, hl, hl.heads, True, True, False)]
     jobs += [(W.HEADLINE, hl, hl.heads, False, False, False)]
@@ -495,6 +502,7 @@ FORMS = (
     ("bf16 Q/K, bf16 V, Q prep separate", False, False, False),
     ("bf16 Q/K, bf16 V, Q prep fused", False, False, True),
     ("int8 Q/K, bf16 V", True, False, False),
+    ("int8 Q/K, bf16 V, Q prep fused", True, False, True),
     ("bf16 Q/K, E4M3 V", False, True, False),
     ("int8 Q/K with K smoothing, E4M3 V", True, True, False),
 )
@@ -638,7 +646,7 @@ def main():
     wl = W.WORKLOADS[cfg]
     int8 = wl.qk_int8 if args.qk is None else args.qk == "int8"
     fp8v = args.pv == "fp8"
-    fused = args.q_prep == "fused" and not (int8 or fp8v)
+    fused = args.q_prep == "fused" and not fp8v
     print(f"[bench] generating {wl.name}: N={wl.n_tokens} H={wl.heads}", file=sys.stderr, flush=True)
     inp = W.make_inputs(cfg, threads=16)
     dev = W.device_inputs(inp)
@@ -655,7 +663,9 @@ def main():
         if timed is not None:
             e0, e1, e2 = ev(), ev(), ev()
             e0.record()
-        if fused:
+        if fused and int8:
+            A.prep_k_i8(p, dev["k"], dev["gamma_k"], dev["pos"], k_out, ks)
+        elif fused:
             A.prep_k(p, dev["k"], dev["gamma_k"], dev["pos"], k_out)
         else:
             A.prep(p, dev["q"], dev["k"], dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
@@ -663,7 +673,9 @@ def main():
             A.prep_v_fp8(p, dev["v"], v_codes, v_scales)
         if timed is not None:
             e1.record()
-        if fused:
+        if fused and int8:
+            A.forward_fused_q_i8(p, dev["q"], dev["gamma_q"], dev["pos"], k_out, ks, dev["v"], o, scale)
+        elif fused:
             A.forward_fused_q(p, dev["q"], dev["gamma_q"], dev["pos"], k_out, dev["v"], o, scale)
         elif fp8v:
             A.forward_fp8v(p, q_out, k_out, v_codes, v_scales, o, scale, qs, ks)
@@ -703,7 +715,7 @@ def main():
     # prep fused into the forward, read K and write K' only
     n, h = wl.n_tokens, wl.heads
     prep_bytes = (1 if fused else 2) * n * h * 128 * 2 + (1 if fused else 2) * n * h * 128 * (1 if int8 else 2) + \
-        (2 * h * ((n + 63) // 64) * 4 if int8 else 0) + \
+        ((1 if fused else 2) * h * ((n + 63) // 64) * 4 if int8 else 0) + \
         (n * h * 128 * 3 + h * 128 * 4 if fp8v else 0)
     dtype = "bf16" if not (int8 or fp8v) else f"{'int8' if int8 else 'bf16'}-qk/{'fp8' if fp8v else 'bf16'}-pv"
 
@@ -728,7 +740,8 @@ def main():
                     "prep_GBps": round(prep_bytes / (prep_ms * 1e-3) / 1e9, 1)},
         "gpu_clock_mhz": clock.summary(),
         "roofline": {"bound": "mfma",
-                     "kernel": "h3attn_forward_fused_q" if fused else "h3attn_forward_fp8v" if fp8v else "h3attn_forward",
+                     "kernel": ("h3attn_forward_fused_q_i8" if int8 else "h3attn_forward_fused_q") if fused
+                     else "h3attn_forward_fp8v" if fp8v else "h3attn_forward",
                      "achieved": round(fwd_tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(fwd_tflops / peak, 4),
                      "traffic": forward_traffic(wl.name, fused) if not (int8 or fp8v) else None,

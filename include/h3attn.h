@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 6
+#define H3ATTN_ABI_VERSION 7
 
 typedef enum {
     H3ATTN_OK = 0,
@@ -304,6 +304,48 @@ int h3attn_forward_fused_q(const h3attn_problem* p,
                            const void* v, int64_t v_stride_tok, int64_t v_stride_head,
                            void* o, int64_t o_stride_tok, int64_t o_stride_head,
                            float softmax_scale, void* stream);
+
+/*
+ * h3attn_prep_k_i8 - the K half of h3attn_prep in the int8 format: writes the
+ * K' codes (int8 [H][N_pad][128], rows n >= N zero) and their per-64-token
+ * block scales (fp32 [H][N_pad / 64]) exactly as h3attn_prep does, and no Q'
+ * ("H3 Runtime Current State", Owned Performance Kernels: K quantization).  It
+ * supplies h3attn_forward_fused_q_i8, which prepares and quantises Q itself.
+ * k, gamma_k, pos_thw: as for h3attn_prep.  k_out, k_scales: device buffers of
+ * h3attn_prepped_qk_bytes and h3attn_scales_bytes; neither may overlap an input
+ * or the other.  Requires qk_format == H3ATTN_QK_I8_BLK64 (E_UNSUPPORTED
+ * otherwise).  Errors: as for h3attn_prep.
+ */
+int h3attn_prep_k_i8(const h3attn_problem* p,
+                     const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                     const void* gamma_k, int64_t gamma_head_stride,
+                     const int32_t* pos_thw, void* k_out, float* k_scales, void* stream);
+
+/*
+ * h3attn_forward_fused_q_i8 - h3attn_forward in the int8 format with the Q
+ * half of h3attn_prep moved into the forward (the entry fusion of the
+ * quantised path, "H3 Runtime Current State", Owned Performance Kernels: the
+ * fused entry kernel; Q quantization): each work-group computes its 256 Q' rows
+ * from raw Q with the prep's arithmetic, rounds them to bf16, and quantises
+ * each 64-row block with the prep's absmax, scale and rounding, so its codes
+ * and scales are those h3attn_prep would write, and the output is that of
+ * h3attn_prep + h3attn_forward bit for bit.  Q' never reaches memory.
+ * q, gamma_q, pos_thw: as for h3attn_prep (raw Q view, its RMSNorm weight,
+ *            the (t, h, w) positions).
+ * k_codes, k_scales: from h3attn_prep_k_i8 (or h3attn_prep) for the same
+ *            descriptor.
+ * v, o, softmax_scale: as for h3attn_forward (bf16 V view); o must not
+ *            overlap any input.
+ * Requires qk_format == H3ATTN_QK_I8_BLK64 (E_UNSUPPORTED otherwise).
+ * Errors: as for h3attn_prep.
+ */
+int h3attn_forward_fused_q_i8(const h3attn_problem* p,
+                              const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                              const void* gamma_q, int64_t gamma_head_stride, const int32_t* pos_thw,
+                              const void* k_codes, const float* k_scales,
+                              const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                              void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                              float softmax_scale, void* stream);
 
 /*
  * h3attn_debug_scores_i32 - test hook for the int8 format: the exact int32

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(path):
 
 
 def test_abi_version_and_status_strings():
-    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 6
+    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 7
     for s in (0, -1, -2, -3, -4, -5, -6, 7):
         assert A.lib.h3attn_status_string(s)
 
@@ -271,6 +271,44 @@ def test_prep_k_checks():
     assert prep_k(p, ko=G + 384 * 10) == -5                 # output on top of k
     assert prep_k(p, ko=I - 64) == -5                       # overlaps positions
     assert prep_k(p, ko=H - 64) == -5                       # overlaps gamma
+
+
+def prep_k_i8(p, k=G, kst=384, ksh=128, gk=H, gsh=0, pos=I, ko=J, ks=K):
+    return A.lib.h3attn_prep_k_i8(ctypes.byref(p), k, kst, ksh, gk, gsh, pos, ko, ks, None)
+
+
+def fwd_fq8(p, q=F, qst=384, qsh=128, gq=H, gsh=0, pos=I, k=G, ks=G + (1 << 32), v=K, vst=384, vsh=128, o=J,
+            ost=384, osh=128, scale=0.088):
+    return A.lib.h3attn_forward_fused_q_i8(ctypes.byref(p), q, qst, qsh, gq, gsh, pos, k, ks, v, vst, vsh, o, ost,
+                                           osh, scale, None)
+
+
+def test_prep_k_i8_checks():
+    p = A.problem(1000, 3, A.QK_I8_BLK64)
+    assert prep_k_i8(A.problem(1000, 3)) == -3                # int8 codes only
+    assert prep_k_i8(A.problem(1000, 3, A.QK_I8_BLK64, head_dim=64)) == -3
+    for kw in ("k", "gk", "pos", "ko", "ks"):
+        assert prep_k_i8(p, **{kw: None}) == -1, kw
+    assert prep_k_i8(p, k=G + 2) == -4
+    assert prep_k_i8(p, ko=J + 8) == -4
+    assert prep_k_i8(p, ks=K + 2) == -4
+    assert prep_k_i8(p, ko=G + 384 * 10) == -5                # codes on top of k
+    assert prep_k_i8(p, ks=H - 64) == -5                      # scales over gamma
+    assert prep_k_i8(p, ks=J + 4096) == -5                    # scales inside the codes
+    assert prep_k_i8(p, ko=K - 64) == -5                      # codes over the scales
+
+
+def test_forward_fused_q_i8_checks():
+    p = A.problem(1000, 3, A.QK_I8_BLK64)
+    assert fwd_fq8(A.problem(1000, 3)) == -3                  # int8 only
+    for kw in ("q", "gq", "pos", "k", "ks", "v", "o"):
+        assert fwd_fq8(p, **{kw: None}) == -1, kw
+    assert fwd_fq8(p, q=F + 2) == -4
+    assert fwd_fq8(p, ks=G + (1 << 32) + 2) == -4
+    assert fwd_fq8(p, scale=0.0) == -2
+    assert fwd_fq8(p, o=F + 384 * 10) == -5                   # output over raw q
+    assert fwd_fq8(p, o=G + (1 << 32)) == -5                  # output over the K scales
+    assert fwd_fq8(p, o=K + 384 * 10) == -5                   # output inside v
 
 
 def test_forward_fused_q_checks():

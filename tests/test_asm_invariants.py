@@ -42,6 +42,7 @@ KERNELS = {
     "ILb0ELb0ELb0ELi8ELb0E": "bf16 Q'/K', bf16 V",
     "ILb0ELb0ELb1ELi8ELb0E": "fused Q prep",
     "ILb1ELb0ELb0ELi8ELb0E": "int8 Q'/K', bf16 V",
+    "ILb1ELb0ELb1ELi8ELb0E": "int8 Q'/K', bf16 V, fused Q prep",
     "ILb0ELb1ELb0ELi8ELb0E": "bf16 Q'/K', E4M3 V",
     "ILb1ELb1ELb0ELi4ELb0E": "int8 Q'/K', E4M3 V (four waves)",
     "ILb1ELb0ELb0ELi8ELb1E": "int32 scores hook, eight waves",

@@ -5,7 +5,7 @@ all memory traffic and a work-group barrier after every LDS stage of the
 forward's tile loop (the K'/V buffer -> LDS fill, the K' operand reads, the V
 operand reads): ``libh3attn_sync.so``.  No stage can overlap another there.
 Its outputs must equal the release build's bit for bit, for every forward
-form and the int32 scores hook, on ragged sizes whose last key tile is
+form (the fused-Q forms included) and the int32 scores hook, on ragged sizes whose last key tile is
 partial, and on a size large enough that every LDS stage is reused many times.
 """
 import numpy as np
@@ -84,6 +84,22 @@ def test_sync_build_bit_identical_int8_and_fp8v(dbg, n, h):
     torch.cuda.synchronize()
     for a, b, what in zip(outs[0], outs[1], ("int8 Q/K", "bf16 Q/K + E4M3 V", "int8 Q/K + E4M3 V")):
         assert same_bits(a, b), what
+
+
+@pytest.mark.parametrize("n,h", SIZES)
+def test_sync_build_bit_identical_int8_fused_q(dbg, n, h):
+    wl, dev = _inputs(n, h, 970 + n)
+    print(f"    N={n} H={h}", flush=True)
+    p8 = problem_for(wl, int8=True)
+    _, k8, _, ks = A.alloc_prepped(p8)
+    A.prep_k_i8(p8, dev["k"], dev["gamma_k"], dev["pos"], k8, ks)
+    outs = []
+    for lib in (A, dbg):
+        o = torch.empty_like(dev["v"])
+        lib.forward_fused_q_i8(p8, dev["q"], dev["gamma_q"], dev["pos"], k8, ks, dev["v"], o, SCALE)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert same_bits(outs[0], outs[1])
 
 
 @pytest.mark.parametrize("n,h", [(4099, 2), (20011, 1)])
