@@ -14,6 +14,12 @@
  *   h3attn_prep     RMSNorm + RoPE of Q and K, written head-major (HND),
  *                   either as bf16 or as int8 codes with per-64-token scales.
  *   h3attn_forward  softmax(Q' K'^T * scale) V, written token-major (NHD).
+ * Around them: h3attn_prep_k + h3attn_forward_fused_q (bf16) and
+ * h3attn_prep_k_i8 + h3attn_forward_fused_q_i8 (int8) move the Q half of the
+ * prep into the forward; h3attn_prep_ksmooth, h3attn_prep_v_fp8 and
+ * h3attn_forward_fp8v complete the quantised path (K smoothing, E4M3 P V);
+ * h3attn_debug_scores_i32 is a test hook and h3attn_calibrate_mfma_bf16 a
+ * measuring aid.
  *
  * Conventions shared by every call
  * --------------------------------
