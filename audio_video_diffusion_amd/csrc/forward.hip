@@ -518,8 +518,10 @@ fwd8_kernel(FwdParams P) {
                 mfma_s_i8(Si[0], a[0][t], q[t], t == 0, bias16);
                 mfma_s_i8(Si[1], a[1][t], q[t], t == 0, bias16);
             }
-            // wait states before the VALU reads the matrix core's results
-            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(Si[0]), "+v"(Si[1]));
+            // wait states before the VALU reads the matrix core's results: 13, one
+            // more than the 12 this compiler pads its own 32x32 products with on
+            // gfx950 (s_nop 11 before a dependent VALU read)
+            asm volatile("s_nop 7\n\ts_nop 4" : "+v"(Si[0]), "+v"(Si[1]));
             debug_stage_sync();
             // the fp32 values 1.5 * 2^23 + S (kI8Bias).  Whole-vector bit casts: a
             // bit cast of a single vector element is miscompiled by this compiler
@@ -545,7 +547,7 @@ fwd8_kernel(FwdParams P) {
                     mfma_s(S[1], a[1][t], q[t], t == 0);
                 }
             }
-            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(S[0]), "+v"(S[1]));
+            asm volatile("s_nop 7\n\ts_nop 4" : "+v"(S[0]), "+v"(S[1]));      // as above
             debug_stage_sync();
         }
         if constexpr (kScores) {

@@ -14,8 +14,9 @@ protocols need:
 * inside each key-tile loop the only vmcnt waits are the kernel's own, none
   of them vmcnt(0) (which would drain the prefetch);
 * every VALU read of a result of an inline-asm matrix-core product comes at
-  least 19 wait states after that product (the gfx950 XDL-write -> VALU-read
-  spacing for a 16-pass product, with one to spare over the 8-pass forms);
+  least 13 wait states after that product (this compiler pads its own 32x32
+  bf16 and int8 products on gfx950 with 12 before a dependent VALU read:
+  s_nop 11; one to spare);
 * every matrix-core product comes at least 2 wait states after the last VALU
   write of any of its source registers (A, B or C; the gfx950 VALU-write ->
   XDL-read spacing, which the compiler enforces only for writes it can see,
@@ -48,7 +49,7 @@ KERNELS = {
     "ILb1ELb0ELb0ELi8ELb1E": "int32 scores hook, eight waves",
     "ILb1ELb1ELb0ELi4ELb1E": "int32 scores hook, four waves",
 }
-MFMA_VALU_WAIT_STATES = 19
+MFMA_VALU_WAIT_STATES = 13
 VALU_MFMA_WAIT_STATES = 2
 SRCC_WAR_WAIT_STATES = 18
 
