@@ -62,11 +62,11 @@ PEAK_HBM_GBS = 8000.0
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
     "kernel": "h3attn_forward_fused_q",
-    "source_sha256": "3dad80699bea3c3e56c5c29c5276424eb50bfff1dcb2493abf87b02abee58719",
+    "source_sha256": "fb2e6abd54917503d44aa83a30e6041d0cd44f3adb1594c09fd4ab9aeae14f4c",
     # the copy's kernel reads 524,319 KiB per 1 GiB as FETCH_SIZE (factor 2.0) and
     # writes 1,048,576 KiB as WRITE_SIZE (factor 1.0)
-    "fetch_kib": 13350841.9, "fetch_scale": 2.0,
-    "write_kib": 821883.2, "write_scale": 1.0,
+    "fetch_kib": 13350844.3, "fetch_scale": 2.0,
+    "write_kib": 819535.6, "write_scale": 1.0,
 }
 
 
