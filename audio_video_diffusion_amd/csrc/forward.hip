@@ -12,13 +12,13 @@
 //   owns one 32-row block and keeps its Q' rows in registers.  Waves w and
 //   w+4 share a SIMD: per wave the state is small (O^T in 64 AGPRs), so two
 //   waves fit each SIMD's register file and the hardware overlaps one wave's
-//   softmax with the other's matrix-core work.  With int8 K' and E4M3 V the
-//   work-group has four waves and 128 rows instead, and two of them share a
-//   CU (see kW);
+//   softmax with the other's matrix-core work.  The int8 forms that read Q'
+//   from the prep run twelve waves and 384 rows instead, three waves per
+//   SIMD (see kW);
 // * the work-group streams K'/V in tiles of 64 keys through four LDS stages,
 //   fetched three tiles ahead with buffer -> LDS DMA (buffer_load_dwordx4 ...
-//   lds: 1 KB per wave instruction, no registers in between; each wave moves
-//   8 of the 64 rows).  K' rows land permuted, V rows stay row-major; 16-byte
+//   lds: 1 KB per wave instruction, no registers in between; waves 0..7 each
+//   move 8 of the 64 rows).  K' rows land permuted, V rows stay row-major; 16-byte
 //   chunks are XOR-swizzled so the operand reads hit every LDS bank.  One
 //   barrier per tile;
 // * everything is computed transposed so that one lane owns one query column:
@@ -250,9 +250,10 @@ __device__ __forceinline__ void wait_vmem_upto() {
 template <bool kInt8, bool kFp8V, int kW>
 struct DmaOffsets8 {
     static constexpr int kRowB = kInt8 ? 128 : 256;   // K' row bytes
-    static constexpr int kRowsPW = 64 / kW;           // K' rows moved per wave
+    static constexpr int kDW = 8;                     // waves 0..7 copy (of 8 or 12)
+    static constexpr int kRowsPW = 64 / kDW;          // K' rows moved per wave
     static constexpr int kN = kRowsPW * kRowB / 1024; // K' DMA instructions per wave
-    static constexpr int kNV = kFp8V ? (128 / kW) * 64 / 1024 : 2;   // V DMA instructions per wave
+    static constexpr int kNV = kFp8V ? (128 / kDW) * 64 / 1024 : 2;   // V DMA instructions per wave
     uint32_t k[kN], v[kNV], vlast[kNV];
     __device__ __forceinline__ DmaOffsets8(int wave, int lane, int64_t v_st, int last_key0, int n) {
         // wave w moves K' rows kRowsPW * w ...: 8 (int8) or 4 (bf16) rows per instruction
@@ -264,11 +265,11 @@ struct DmaOffsets8 {
             k[r] = (uint32_t)((kFp8V ? key_of_row_f8(rho) : key_of_row(rho)) * kRowB + c * 16);
         }
         if constexpr (kFp8V) {
-            // E4M3 V^T tile [128 d][64 keys]: wave w moves d-rows (128 / kW) w ...,
+            // E4M3 V^T tile [128 d][64 keys]: wave w moves d-rows 16 w ...,
             // 16 per instruction; LDS slot s of row d holds 16-byte chunk s ^ ((d >> 2) & 3)
 #pragma unroll
             for (int r = 0; r < kNV; ++r) {
-                const int d = (128 / kW) * wave + 16 * r + (lane >> 2);
+                const int d = (128 / kDW) * wave + 16 * r + (lane >> 2);
                 const int c = (lane & 3) ^ ((d >> 2) & 3);
                 v[r] = vlast[r] = (uint32_t)(d * 64 + c * 16);
             }
@@ -308,12 +309,15 @@ constexpr float kPLog2Fp8 = 0.8f;
 // Q'K'^T chain then starts from -m, so the scores leave the matrix core ready
 // for exp2.  Int8 format: rounded to bf16 and quantised per 64-row block
 // exactly as the prep does (codes and scales identical), then the int8 path.
-// kW = 4 (int8 K' with E4M3 V only): four waves own 128 query rows and the
-// stages take 64 KB of LDS, so two independent work-groups share each CU (one
-// wave of each per SIMD).  Their barriers are unrelated, so the two waves of a
-// SIMD drift out of phase and one's softmax covers the other's matrix-core
-// phases, also at the tile edges where the eight-wave form keeps them in step;
-// each row's arithmetic is unchanged.
+// kW = 12 (int8 Q'/K' read from the prep, bf16 or E4M3 V): twelve waves, three
+// per SIMD, own 384 query rows.  The int8 state is small enough (Q' codes in
+// 16 registers, K' operands half the bf16 size) for three waves in a SIMD's
+// register file, 168 registers each; the K'/V stream then serves 384 queries
+// instead of 256 (a third fewer L2 -> LDS bytes per FLOP) and each SIMD has a
+// third wave to issue from.  Waves 0..7 issue the copies exactly as in the
+// eight-wave form, so the LDS layout is unchanged, and each row's arithmetic
+// is unchanged (outputs bit-identical).  The bf16 forms need more than 168
+// registers and keep eight waves.
 // kScores (int8 only; the test hook h3attn_debug_scores_i32): the kernel runs
 // its own Q'K'^T path -- Q' codes in registers, the K' stream with its DMA
 // offsets and LDS row permutation, the int8 product chain from the
@@ -321,13 +325,13 @@ constexpr float kPLog2Fp8 = 0.8f;
 // writes the exact int32 scores of the window in place of the softmax and the
 // P V product (no V is fetched).
 template <bool kInt8, bool kFp8V, bool kFuseQ = false, int kW = 8, bool kScores = false>
-__global__ void __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kW / 4, kW / 4)))
 fwd8_kernel(FwdParams P) {
     static_assert(!(kFuseQ && (kFp8V || kScores || kW != 8)), "the fused Q prologue: bf16 V, eight waves");
     // fused Q in the bf16 format: Q' carries the logit scale and the chains start
     // from -m (the int8 form quantises Q' as the prep does and runs the int8 path)
     constexpr bool kFuseBf = kFuseQ && !kInt8;
-    static_assert(kW == 8 || (kW == 4 && kInt8 && kFp8V), "four waves: int8 K' with E4M3 V only");
+    static_assert(kW == 8 || (kW == 12 && kInt8 && !kFuseQ), "twelve waves: int8 Q'/K' from the prep");
     static_assert(!kScores || kInt8, "the scores hook covers the int8 Q'K'^T path");
     constexpr int kBMw = 32 * kW;                  // query rows per work-group
     using D = DmaOffsets8<kInt8, kFp8V, kW>;
@@ -388,7 +392,8 @@ fwd8_kernel(FwdParams P) {
     if constexpr (!kFuseQ) {
 #pragma unroll
         for (int t = 0; t < kSteps; ++t)
-            q[t] = __builtin_bit_cast(QOp, ld16(qhead + (int64_t)(q0 + n32) * D::kRowB + 32 * t + 16 * hh));
+            // rows past the padded tensor (384-row tiles) load row npad - 1: never stored
+            q[t] = __builtin_bit_cast(QOp, ld16(qhead + (int64_t)min(q0 + n32, P.npad - 1) * D::kRowB + 32 * t + 16 * hh));
     }
     // Fused Q: thread (r = tid / 8, slot tid % 8) prepares rows r + 64 ps,
     // ps = 0..3, of the work-group's 256; its raw Q chunks, positions, gamma
@@ -458,9 +463,11 @@ fwd8_kernel(FwdParams P) {
     const int last = kScores ? P.kt1 : ntiles - 1;
     const bool ragged = (n % kBN) != 0 && last == ntiles - 1;
 
-    const D dmo(wave, lane, P.v_st, last * kBN, n);
+    const D dmo(wave & 7, lane, P.v_st, last * kBN, n);     // waves 8..11 copy nothing
     float ks_cur = kInt8 && !kScores ? kscale[0] : 1.f;
     auto fetch = [&](int t) {
+        if constexpr (kW > D::kDW)
+            if (wave >= D::kDW) return;
         const int kt = min(t, last);
         const u32x4 kr = raw_rsrc(khead + (int64_t)kt * kKTileB);
 #pragma unroll
@@ -855,13 +862,14 @@ fwd8_kernel(FwdParams P) {
     }
     wait_vmem_upto<(kAhead - 1) * kDma8>();
     __syncthreads();
-    // Fused Q and int8 Q'/K' with bf16 V run the loop unrolled by the four
-    // stages, so that each stage's LDS offsets are immediates of the operand
-    // reads (fewer address adds per tile): measured -1.8% and -0.7% there
-    // (same process and box, outputs bit-identical); the other forms were
-    // slower so (bf16 +1.5%, bf16 Q'/K' with E4M3 V +4.6%, int8 with E4M3 V
-    // +-1%) and keep the rolled loop.
-    constexpr bool kUnroll = kW == 8 && (kFuseQ || (kInt8 && !kFp8V));
+    // The fused-Q forms run the loop unrolled by the four stages, so that each
+    // stage's LDS offsets are immediates of the operand reads (fewer address
+    // adds per tile): measured -1.8% for bf16 and -0.7% for int8 Q'/K' with
+    // bf16 V in the eight-wave form (same process and box, outputs
+    // bit-identical); the other eight-wave forms were slower so (bf16 +1.5%,
+    // bf16 Q'/K' with E4M3 V +4.6%), and the twelve-wave forms spill unrolled
+    // (168 registers), so these keep the rolled loop.
+    constexpr bool kUnroll = kFuseQ;
     int j = jb;
     if constexpr (kUnroll) {
         for (; j < last && (j & 3); ++j) tile(j, false, j & 3);
@@ -908,10 +916,11 @@ fwd8_kernel(FwdParams P) {
 hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
     const dim3 grid(kXcds * P.per_xcd), block(512);
-    if (int8 && fp8v)      // four waves, 128-row tiles (forward_tile_rows), plain block order
-        hipLaunchKernelGGL((fwd8_kernel<true, true, false, 4>), dim3(P.total), dim3(256), 0, stream, P);
+    // int8: twelve waves, 384-row tiles (forward_tile_rows), plain block order
+    if (int8 && fp8v)
+        hipLaunchKernelGGL((fwd8_kernel<true, true, false, 12>), dim3(P.total), dim3(768), 0, stream, P);
     else if (int8)
-        hipLaunchKernelGGL((fwd8_kernel<true, false>), grid, block, 0, stream, P);
+        hipLaunchKernelGGL((fwd8_kernel<true, false, false, 12>), dim3(P.total), dim3(768), 0, stream, P);
     else if (fp8v)
         hipLaunchKernelGGL((fwd8_kernel<false, true>), grid, block, 0, stream, P);
     else
@@ -928,18 +937,19 @@ hipError_t launch_forward_fused_q(const FwdParams& P, bool int8, hipStream_t str
     return hipGetLastError();
 }
 
-int forward_tile_rows(bool int8, bool fp8v) { return int8 && fp8v ? 128 : kBM; }
+int forward_tile_rows(bool int8) { return int8 ? 384 : kBM; }
 
-// The int8 forward's own Q'K'^T path over a window (kScores): `fp8v_layout`
-// picks the four-wave form of the E4M3-V forward (its K' row order) instead of
-// the eight-wave form.  P.total work-groups take query tiles s_qt0.. of head
-// s_head; key tiles kt0..kt1 stream through the stages.
+// The int8 forward's own Q'K'^T path over a window (kScores), in the
+// twelve-wave form the int8 forwards run: `fp8v_layout` picks the K' row
+// order of the E4M3-V forward instead of the bf16-V one.  P.total work-groups
+// take query tiles s_qt0.. of head s_head; key tiles kt0..kt1 stream through
+// the stages.
 hipError_t launch_scores_i8(const FwdParams& P, bool fp8v_layout, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
     if (fp8v_layout)
-        hipLaunchKernelGGL((fwd8_kernel<true, true, false, 4, true>), dim3(P.total), dim3(256), 0, stream, P);
+        hipLaunchKernelGGL((fwd8_kernel<true, true, false, 12, true>), dim3(P.total), dim3(768), 0, stream, P);
     else
-        hipLaunchKernelGGL((fwd8_kernel<true, false, false, 8, true>), dim3(P.total), dim3(512), 0, stream, P);
+        hipLaunchKernelGGL((fwd8_kernel<true, false, false, 12, true>), dim3(P.total), dim3(768), 0, stream, P);
     return hipGetLastError();
 }
 

@@ -59,7 +59,7 @@ hipError_t launch_prep_k(const PrepParams& P, bool int8, hipStream_t stream);
 hipError_t launch_prep_ksmooth(const PrepParams& P, hipStream_t stream);
 hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t stream);
 // query rows per work-group of that forward (FwdParams::qtiles counts tiles of this size)
-int forward_tile_rows(bool int8, bool fp8v);
+int forward_tile_rows(bool int8);
 // bf16 Q'/K', V through its view, Q' computed from raw Q in the prologue
 hipError_t launch_forward_fused_q(const FwdParams& P, bool int8, hipStream_t stream);
 hipError_t launch_prep_v(const PrepVParams& P, hipStream_t stream);

@@ -311,7 +311,7 @@ def debug_scores_i32(p: Problem, q_codes, k_codes, head: int, row0: int, nrows: 
                      ncols: int, out, stream=None, fp8v_layout: int = 0):
     """``h3attn_debug_scores_i32`` into ``out`` (int32 [nrows, ncols], contiguous).
 
-    ``fp8v_layout`` 1 runs the four-wave kernel of the int8 + E4M3-V forward."""
+    ``fp8v_layout`` 1 runs the kernel of the int8 + E4M3-V forward (its K' row order)."""
     rc = _lib.h3attn_debug_scores_i32(ctypes.byref(p), _ptr(q_codes), _ptr(k_codes), head, row0,
                                       nrows, col0, ncols, fp8v_layout, _ptr(out), _stream(stream))
     if rc:

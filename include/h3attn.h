@@ -365,10 +365,10 @@ int h3attn_forward_fused_q_i8(const h3attn_problem* p,
  * in place of the softmax (V is not read).
  *   out[r][c] = sum_d q_codes[head][row0 + r][d] * k_codes[head][col0 + c][d]
  * for r < nrows, c < ncols (out is int32 [nrows][ncols], row-major, device).
- * fp8v_layout: 0 = the form h3attn_forward runs (eight waves, 256 query rows
- *            per work-group), 1 = the form h3attn_forward_fp8v runs with int8
- *            Q'/K' (four waves, 128 rows, the K' row order of the FP8 P V
- *            product).
+ * fp8v_layout: 0 = the form h3attn_forward runs, 1 = the form
+ *            h3attn_forward_fp8v runs with int8 Q'/K' (the K' row order of the
+ *            FP8 P V product); both run twelve waves, 384 query rows per
+ *            work-group.
  * Requires the int8 format, 0 <= head < H, nrows, ncols >= 1,
  * 0 <= row0, row0 + nrows <= N, 0 <= col0, col0 + ncols <= N,
  * fp8v_layout in {0, 1} (E_SHAPE otherwise).

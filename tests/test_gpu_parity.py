@@ -325,8 +325,8 @@ def _check_scores(p8, q8, k8, heads, windows, layouts=(0, 1)):
 
 @pytest.mark.parametrize("cfg,n,h", [(0, None, None), (41, 4099, 2), (42, 129, 1), (43, 1, 1)])
 def test_int8_scores_i32_bit_exact(cfg, n, h):
-    # the int8 forward kernels' own Q'K'^T path (eight-wave form and the
-    # four-wave form of the E4M3-V forward) against exact integer products
+    # the int8 forward kernels' own Q'K'^T path (the bf16-V and the E4M3-V
+    # forms' K' row orders) against exact integer products
     wl = W.WORKLOADS[0] if n is None else W.ragged_workload(n, h)
     inp = W.make_inputs(cfg, wl)
     _, _, p8, _, _, q8, k8, _, _ = _prep_both(wl, inp)
