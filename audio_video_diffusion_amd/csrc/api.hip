@@ -319,7 +319,7 @@ int forward_common(const h3attn_problem* p, const void* q_prep, const void* k_pr
     P.vs = v_scales;
     P.o = static_cast<uint16_t*>(o); P.o_st = o_stride_tok; P.o_sh = o_stride_head;
     P.n = (int)n; P.h = (int)h; P.npad = (int)npad_of(p); P.nblk = (int)nblk_of(p);
-    const int tile_rows = rq ? 256 : h3::forward_tile_rows(i8);
+    const int tile_rows = h3::forward_tile_rows(i8);
     P.qtiles = (int)((n + tile_rows - 1) / tile_rows);
     const int64_t total = h * P.qtiles;
     if (total > ((int64_t)1 << 28)) return H3ATTN_E_SHAPE;

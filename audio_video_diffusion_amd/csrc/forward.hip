@@ -54,7 +54,7 @@
 
 namespace h3 {
 
-constexpr int kBM = 256;            // query rows per work-group
+constexpr int kBM = 256;            // query rows per work-group of eight waves
 constexpr int kBN = 64;             // keys per tile
 constexpr int kXcds = 8;
 constexpr float kRescaleLog2 = 8.0f;
@@ -130,6 +130,13 @@ __device__ __forceinline__ u32x4 raw_rsrc(const void* base) {
 __device__ __forceinline__ void dma16_buf(const u32x4& rsrc, uint32_t voff, uint32_t lds_dst) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_dst)) : "memory", "m0");
+}
+// The same with a scalar byte offset added to every lane's offset (both
+// non-negative, their sum below 2^32).
+__device__ __forceinline__ void dma16_buf_so(const u32x4& rsrc, uint32_t voff, uint32_t soff, uint32_t lds_dst) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_dst)),
+                    "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -254,8 +261,11 @@ struct DmaOffsets8 {
     static constexpr int kRowsPW = 64 / kDW;          // K' rows moved per wave
     static constexpr int kN = kRowsPW * kRowB / 1024; // K' DMA instructions per wave
     static constexpr int kNV = kFp8V ? (128 / kDW) * 64 / 1024 : 2;   // V DMA instructions per wave
-    uint32_t k[kN], v[kNV], vlast[kNV];
-    __device__ __forceinline__ DmaOffsets8(int wave, int lane, int64_t v_st, int last_key0, int n) {
+    // bf16 V: the second copy's offsets are the first's plus 4 rows (a scalar
+    // offset), so only the first is kept
+    static constexpr int kNVo = kFp8V ? kNV : 1;
+    uint32_t k[kN], v[kNVo];
+    __device__ __forceinline__ DmaOffsets8(int wave, int lane, int64_t v_st) {
         // wave w moves K' rows kRowsPW * w ...: 8 (int8) or 4 (bf16) rows per instruction
         constexpr int cpr = kRowB / 16, rpi = 64 / cpr;
 #pragma unroll
@@ -271,17 +281,15 @@ struct DmaOffsets8 {
             for (int r = 0; r < kNV; ++r) {
                 const int d = (128 / kDW) * wave + 16 * r + (lane >> 2);
                 const int c = (lane & 3) ^ ((d >> 2) & 3);
-                v[r] = vlast[r] = (uint32_t)(d * 64 + c * 16);
+                v[r] = (uint32_t)(d * 64 + c * 16);
             }
         } else {
+            // wave w moves V rows 8 w + 4 r + lane / 16, r = 0, 1 (the chunk
+            // swizzle is the same for both r)
             const uint32_t rs = (uint32_t)(v_st * 2);
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int kappa = 8 * wave + 4 * r + (lane >> 4);
-                const int c = (lane & 15) ^ (4 * (kappa & 3));
-                v[r] = (uint32_t)kappa * rs + c * 16;
-                vlast[r] = (uint32_t)min(kappa, n - 1 - last_key0) * rs + c * 16;
-            }
+            const int kappa = 8 * wave + (lane >> 4);
+            const int c = (lane & 15) ^ (4 * (kappa & 3));
+            v[0] = (uint32_t)kappa * rs + c * 16;
         }
     }
 };
@@ -327,11 +335,11 @@ constexpr float kPLog2Fp8 = 0.8f;
 template <bool kInt8, bool kFp8V, bool kFuseQ = false, int kW = 8, bool kScores = false>
 __global__ void __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kW / 4, kW / 4)))
 fwd8_kernel(FwdParams P) {
-    static_assert(!(kFuseQ && (kFp8V || kScores || kW != 8)), "the fused Q prologue: bf16 V, eight waves");
+    static_assert(!(kFuseQ && (kFp8V || kScores)), "the fused Q prologue: bf16 V");
     // fused Q in the bf16 format: Q' carries the logit scale and the chains start
     // from -m (the int8 form quantises Q' as the prep does and runs the int8 path)
     constexpr bool kFuseBf = kFuseQ && !kInt8;
-    static_assert(kW == 8 || (kW == 12 && kInt8 && !kFuseQ), "twelve waves: int8 Q'/K' from the prep");
+    static_assert(kW == 8 || (kW == 12 && kInt8), "twelve waves: int8 Q'/K' only");
     static_assert(!kScores || kInt8, "the scores hook covers the int8 Q'K'^T path");
     constexpr int kBMw = 32 * kW;                  // query rows per work-group
     using D = DmaOffsets8<kInt8, kFp8V, kW>;
@@ -395,17 +403,18 @@ fwd8_kernel(FwdParams P) {
             // rows past the padded tensor (384-row tiles) load row npad - 1: never stored
             q[t] = __builtin_bit_cast(QOp, ld16(qhead + (int64_t)min(q0 + n32, P.npad - 1) * D::kRowB + 32 * t + 16 * hh));
     }
-    // Fused Q: thread (r = tid / 8, slot tid % 8) prepares rows r + 64 ps,
-    // ps = 0..3, of the work-group's 256; its raw Q chunks, positions, gamma
+    // Fused Q: thread (r = tid / 8, slot tid % 8) prepares rows r + kBMw / 4 * ps,
+    // ps = 0..3, of the work-group's kBMw; its raw Q chunks, positions, gamma
     // and the slot's RoPE frequencies are loaded here, before the K'/V stream
     // starts (see the wait below).
+    constexpr int kPsRows = kBMw / 4;              // rows per ps: 64 or 96
     const Slot fsl = slot_of(tid & 7, P.sec0, P.sec1, P.sec2);
     u32x4 fqa[4], fqb[4], fga, fgb;
     double fpv[4], ffreq[8];
     if constexpr (kFuseQ) {
 #pragma unroll
         for (int ps = 0; ps < 4; ++ps) {
-            const int tok = qt * kBM + 64 * ps + (tid >> 3);
+            const int tok = qt * kBMw + kPsRows * ps + (tid >> 3);
             if (tok < n) {
                 const uint16_t* qr = P.qraw + (int64_t)tok * P.q_st + (int64_t)head * P.q_sh;
                 fqa[ps] = ld16(qr + 8 * fsl.a);
@@ -429,10 +438,11 @@ fwd8_kernel(FwdParams P) {
     // (up to 15 for a 32x32 product) can reach it first.  The compiler cannot
     // see that for a product in asm; it would rebuild the chain-start values
     // (bias16 here, negm in the fused form) before each chain and hand their
-    // registers to other values right after it.  Made opaque here and used
-    // again after the tile loop, they stay in registers, untouched by anything
-    // but their own updates, for the whole loop.
-    asm volatile("" : "+v"(bias16));
+    // registers to other values right after it.  Made opaque (here, or for
+    // the fused int8 form after its prologue, which needs the registers) and
+    // used again after the tile loop, they stay in registers, untouched by
+    // anything but their own updates, for the whole loop.
+    if constexpr (!(kFuseQ && kInt8)) asm volatile("" : "+v"(bias16));
     if constexpr (kInt8 && !kScores && !kFuseQ) qscale = q0 < n ? P.qs[(int64_t)head * P.nblk + q0 / kQuantBlock] : 0.f;
     // K block scales through the constant address space: one scalar load per
     // tile, counted by lgkmcnt.  A vector load would be waited for with
@@ -463,7 +473,7 @@ fwd8_kernel(FwdParams P) {
     const int last = kScores ? P.kt1 : ntiles - 1;
     const bool ragged = (n % kBN) != 0 && last == ntiles - 1;
 
-    const D dmo(wave & 7, lane, P.v_st, last * kBN, n);     // waves 8..11 copy nothing
+    const D dmo(wave & 7, lane, P.v_st);     // waves 8..11 copy nothing
     float ks_cur = kInt8 && !kScores ? kscale[0] : 1.f;
     auto fetch = [&](int t) {
         if constexpr (kW > D::kDW)
@@ -482,10 +492,25 @@ fwd8_kernel(FwdParams P) {
             for (int r = 0; r < D::kNV; ++r) dma16_buf(vr, dmo.v[r], vbuf_addr(t) + 1024 * (D::kNV * wave + r));
         } else {
             const u32x4 vr = raw_rsrc(vhead + (int64_t)kt * kBN * P.v_st * 2);
-            const bool lt = kt == last;
+            const uint32_t rs = (uint32_t)(P.v_st * 2);
+            if (kt == last) {
+                // the last tile's V rows past N are clamped to row N - 1 (their P
+                // is 0): the offsets are formed here, from an opaque copy of the
+                // lane index, rather than kept in registers through the loop
+                const int kmax = n - 1 - last * kBN;
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
 #pragma unroll
-            for (int r = 0; r < 2; ++r)
-                dma16_buf(vr, lt ? dmo.vlast[r] : dmo.v[r], vbuf_addr(t) + (8 * wave + 4 * r) * 256);
+                for (int r = 0; r < 2; ++r) {
+                    const int kappa = 8 * wave + 4 * r + (ln >> 4);
+                    const int c = (ln & 15) ^ (4 * (kappa & 3));
+                    const uint32_t off = (uint32_t)min(kappa, kmax) * rs + c * 16;
+                    dma16_buf(vr, off, vbuf_addr(t) + (8 * wave + 4 * r) * 256);
+                }
+            } else {
+                dma16_buf(vr, dmo.v[0], vbuf_addr(t) + (8 * wave) * 256);
+                dma16_buf_so(vr, dmo.v[0], 4 * rs, vbuf_addr(t) + (8 * wave + 4) * 256);
+            }
         }
     };
 
@@ -746,9 +771,13 @@ fwd8_kernel(FwdParams P) {
         if (!behind) tile_sync();
     };
 
-    fetch(jb);
-    fetch(jb + 1);
-    if constexpr (kAhead == 3) fetch(jb + 2);
+    // the first tiles stream in while Q' is prepared (the int8 form prepares
+    // it first: its prologue needs the registers)
+    if constexpr (!(kFuseQ && kInt8)) {
+        fetch(jb);
+        fetch(jb + 1);
+        if constexpr (kAhead == 3) fetch(jb + 2);
+    }
     if constexpr (kFuseBf) {
         // Q' of the work-group's 256 rows, computed while tiles 0..2 stream
         // in, in two halves of 128 rows staged through LDS stage 3 (K' part:
@@ -771,7 +800,7 @@ fwd8_kernel(FwdParams P) {
                 u32x4 oa, ob;
                 // Q' is rounded to bf16 once, with the base-2 logit scale folded in
                 norm_rotate<true>(xa, xb, ga, gb, cs, sn, P.eps, oa, ob, ra, rb, P.c);
-                if (qt * kBM + 64 * ps + r >= n) oa = ob = u32x4{0, 0, 0, 0};
+                if (qt * kBMw + kPsRows * ps + r >= n) oa = ob = u32x4{0, 0, 0, 0};
                 uint8_t* st = (s == 0 ? kbuf(3) : vbuf(3)) + r * 256;
                 *reinterpret_cast<u32x4*>(st + ((fsl.a ^ (r & 15)) * 16)) = oa;
                 *reinterpret_cast<u32x4*>(st + ((fsl.b ^ (r & 15)) * 16)) = ob;
@@ -790,18 +819,25 @@ fwd8_kernel(FwdParams P) {
         }
     }
     if constexpr (kFuseQ && kInt8) {
-        // Int8 Q': the work-group's 256 rows are four 64-row quantisation
-        // blocks; thread (r = tid / 8, slot tid % 8) prepares row r of each.
-        // Per half (blocks 2h, 2h + 1): Q' rounded to bf16 exactly as the prep
-        // does, the block absmax over the work-group, the prep's scale and
-        // codes, staged through V stage 3 (128 int8 rows, 16-byte chunks
-        // XOR-swizzled as the K' tiles); waves 4h..4h+3 take their operands and
-        // their block's scale from half h.
+        // Int8 Q': the work-group's kBMw rows are 64-row quantisation blocks;
+        // thread (r = tid / 8, slot tid % 8) prepares rows r + kPsRows ps.  Per
+        // half (ps = 2h, 2h + 1: rows rho = r + kPsRows s of the half, s = 0, 1,
+        // two or three blocks): Q' rounded to bf16 exactly as the prep does,
+        // the block absmax over the work-group, the prep's scale and codes,
+        // staged through stage 3 (half row rho < 64 in the K' part, the rest in
+        // the V part; 128-byte rows, 16-byte chunks XOR-swizzled as the K'
+        // tiles).  A wave's 8 rows of one ps lie in one block, so per wave and
+        // ps one absmax goes to LDS.  Wave w's 32 rows belong to half
+        // w / (kW / 2); it takes its operands and its block's scale there.
+        constexpr int kHalfRows = kBMw / 2, kBlkPerHalf = kHalfRows / 64, kWPerHalf = kW / 2;
+        __shared__ float red[kW][2];                              // [wave][s]
         float ga[8], gb[8];
         unpack8(fga, ga);
         unpack8(fgb, gb);
         const int r = tid >> 3;
-        float* red = reinterpret_cast<float*>(kbuf(3));          // [8 waves][2 blocks]
+        auto stage_row = [&](int rho) {
+            return rho < 64 ? kbuf(3) + rho * 128 : vbuf(3) + (rho - 64) * 128;
+        };
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             float rv[2][16];
@@ -818,47 +854,65 @@ fwd8_kernel(FwdParams P) {
                 mx[s] = 0.f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    if (qt * kBM + 64 * ps + r >= n) rv[s][i] = 0.f;
+                    if (qt * kBMw + kPsRows * ps + r >= n) rv[s][i] = 0.f;
                     mx[s] = fmaxf(mx[s], fabsf(rv[s][i]));
                 }
 #pragma unroll
                 for (int sh = 1; sh < 64; sh <<= 1) mx[s] = fmaxf(mx[s], __shfl_xor(mx[s], sh));
             }
             if (lane == 0) {
-                red[2 * wave] = mx[0];
-                red[2 * wave + 1] = mx[1];
+                red[wave][0] = mx[0];
+                red[wave][1] = mx[1];
             }
             __syncthreads();
-            float inv[2];
+            // absmax of each block of the half: the partials of the (wave, s)
+            // whose rows 8 wave + kPsRows s .. + 7 fall in it
+            float amax[kBlkPerHalf];
+#pragma unroll
+            for (int b = 0; b < kBlkPerHalf; ++b) {
+                amax[b] = 0.f;
+#pragma unroll
+                for (int w = 0; w < kW; ++w)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        if (((8 * w + kPsRows * s) >> 6) == b) amax[b] = fmaxf(amax[b], red[w][s]);
+            }
+            // IEEE fp32 divisions, as in the prep (no fast-math in this library).
+            // The scale is uniform over the wave: kept in a scalar register.
+            if (wave / kWPerHalf == half)
+                qscale = __int_as_float(__builtin_amdgcn_readfirstlane(
+                    __float_as_int(amax[(wave % kWPerHalf) >> 1] / 127.0f)));
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                float a = red[s];
-#pragma unroll
-                for (int w = 1; w < 8; ++w) a = fmaxf(a, red[2 * w + s]);
-                // IEEE fp32 divisions, as in the prep (no fast-math in this library)
-                if ((wave >> 2) == half && ((wave >> 1) & 1) == s) qscale = a / 127.0f;
-                inv[s] = a > 0.f ? 127.0f / a : 0.f;
-                const int row = 64 * s + r;                        // row of the half
-                uint8_t* st = vbuf(3) + row * 128;
-                const int sw = k_swizzle<true>(row);
+                const int rho = kPsRows * s + r;                   // row of the half
+                const float a = amax[(8 * wave + kPsRows * s) >> 6];
+                const float inv = a > 0.f ? 127.0f / a : 0.f;
+                uint8_t* st = stage_row(rho);
+                const int sw = k_swizzle<true>(rho);
                 const Slot& sl = fsl;
                 *reinterpret_cast<u32x2*>(st + (((sl.a >> 1) ^ sw) * 16) + (sl.a & 1) * 8) =
-                    u32x2{quant4(rv[s], inv[s]), quant4(rv[s] + 4, inv[s])};
+                    u32x2{quant4(rv[s], inv), quant4(rv[s] + 4, inv)};
                 *reinterpret_cast<u32x2*>(st + (((sl.b >> 1) ^ sw) * 16) + (sl.b & 1) * 8) =
-                    u32x2{quant4(rv[s] + 8, inv[s]), quant4(rv[s] + 12, inv[s])};
+                    u32x2{quant4(rv[s] + 8, inv), quant4(rv[s] + 12, inv)};
             }
             __syncthreads();
-            if ((wave >> 2) == half) {
-                const int row = (wave & 3) * 32 + n32;            // row of the half
-                const uint8_t* src = vbuf(3) + row * 128;
+            if (wave / kWPerHalf == half) {
+                const int rho = (wave % kWPerHalf) * 32 + n32;    // row of the half
+                const uint8_t* src = stage_row(rho);
 #pragma unroll
                 for (int t = 0; t < kSteps; ++t)
-                    q[t] = *reinterpret_cast<const QOp*>(src + (((2 * t + hh) ^ k_swizzle<true>(row)) * 16));
+                    q[t] = *reinterpret_cast<const QOp*>(src + (((2 * t + hh) ^ k_swizzle<true>(rho)) * 16));
             }
             // the staging reads are complete before stage 3 is written again
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __syncthreads();
         }
+    }
+    if constexpr (kFuseQ && kInt8) {
+        asm volatile("" : "+v"(bias16));
+        fetch(jb);
+        fetch(jb + 1);
+        fetch(jb + 2);
     }
     wait_vmem_upto<(kAhead - 1) * kDma8>();
     __syncthreads();
@@ -869,7 +923,7 @@ fwd8_kernel(FwdParams P) {
     // bit-identical); the other eight-wave forms were slower so (bf16 +1.5%,
     // bf16 Q'/K' with E4M3 V +4.6%), and the twelve-wave forms spill unrolled
     // (168 registers), so these keep the rolled loop.
-    constexpr bool kUnroll = kFuseQ;
+    constexpr bool kUnroll = kFuseQ && kW == 8;
     int j = jb;
     if constexpr (kUnroll) {
         for (; j < last && (j & 3); ++j) tile(j, false, j & 3);
@@ -930,8 +984,8 @@ hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t 
 
 hipError_t launch_forward_fused_q(const FwdParams& P, bool int8, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
-    if (int8)
-        hipLaunchKernelGGL((fwd8_kernel<true, false, true>), dim3(P.total), dim3(512), 0, stream, P);
+    if (int8)      // twelve waves, 384-row tiles (forward_tile_rows), plain block order
+        hipLaunchKernelGGL((fwd8_kernel<true, false, true, 12>), dim3(P.total), dim3(768), 0, stream, P);
     else
         hipLaunchKernelGGL((fwd8_kernel<false, false, true>), dim3(kXcds * P.per_xcd), dim3(512), 0, stream, P);
     return hipGetLastError();

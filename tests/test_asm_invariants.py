@@ -43,7 +43,7 @@ KERNELS = {
     "ILb0ELb0ELb0ELi8ELb0E": "bf16 Q'/K', bf16 V",
     "ILb0ELb0ELb1ELi8ELb0E": "fused Q prep",
     "ILb1ELb0ELb0ELi12ELb0E": "int8 Q'/K', bf16 V (twelve waves)",
-    "ILb1ELb0ELb1ELi8ELb0E": "int8 Q'/K', bf16 V, fused Q prep",
+    "ILb1ELb0ELb1ELi12ELb0E": "int8 Q'/K', bf16 V, fused Q prep (twelve waves)",
     "ILb0ELb1ELb0ELi8ELb0E": "bf16 Q'/K', E4M3 V",
     "ILb1ELb1ELb0ELi12ELb0E": "int8 Q'/K', E4M3 V (twelve waves)",
     "ILb1ELb0ELb0ELi12ELb1E": "int32 scores hook, bf16-V K' order",
@@ -117,10 +117,10 @@ def test_all_forms_present(kernels):
     assert set(kernels) == set(KERNELS)
 
 
-# Twelve-wave forms (168 registers per wave): a few lane-derived values that
-# only the ragged last tile and the epilogue use after the loop are kept in
-# scratch; nothing inside a loop touches it.
-SCRATCH_OUTSIDE_LOOPS = {"ILb1ELb0ELb0ELi12ELb0E", "ILb1ELb1ELb0ELi12ELb0E"}
+# Twelve-wave forms (168 registers per wave) that keep a few values in
+# scratch outside the tile loop (lane-derived values that only the ragged last
+# tile and the epilogue use, prologue state); nothing inside a loop touches it.
+SCRATCH_OUTSIDE_LOOPS = {"ILb1ELb1ELb0ELi12ELb0E", "ILb1ELb0ELb1ELi12ELb0E"}
 
 
 def loop_lines(body):
@@ -142,7 +142,7 @@ def test_no_scratch(kernels, key):
     if key in SCRATCH_OUTSIDE_LOOPS:
         size = next(int(m.group(1)) for ln in meta
                     for m in [re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", ln)] if m)
-        assert size <= 32, (KERNELS[key], size)
+        assert size <= 64, (KERNELS[key], size)
         loops = loop_lines(body)
         assert loops, KERNELS[key]
         assert not loops.intersection(scratch), KERNELS[key]
