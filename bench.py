@@ -62,11 +62,11 @@ PEAK_HBM_GBS = 8000.0
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
     "kernel": "h3attn_forward_fused_q",
-    "source_sha256": "fb2e6abd54917503d44aa83a30e6041d0cd44f3adb1594c09fd4ab9aeae14f4c",
+    "source_sha256": "9c7b9f105179e2c7acbe6ca0c21161b715270b57572416db9e50dba682155a05",
     # the copy's kernel reads 524,319 KiB per 1 GiB as FETCH_SIZE (factor 2.0) and
     # writes 1,048,576 KiB as WRITE_SIZE (factor 1.0)
-    "fetch_kib": 13350844.3, "fetch_scale": 2.0,
-    "write_kib": 819535.6, "write_scale": 1.0,
+    "fetch_kib": 13350854.3, "fetch_scale": 2.0,
+    "write_kib": 820275.2, "write_scale": 1.0,
 }
 
 
