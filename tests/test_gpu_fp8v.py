@@ -128,7 +128,7 @@ def test_prep_v_fp8_strided_view_zero_channel_and_reuse():
 # forward: small cases, every output element
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("n", [None, 1, 2, 63, 64, 65, 129, 257, 1000, 4099])
+@pytest.mark.parametrize("n", [None, 1, 2, 63, 64, 65, 129, 257, 385, 1000, 4099])
 @pytest.mark.parametrize("int8", [False, True])
 def test_forward_fp8v_matches_oracle(n, int8):
     wl = W.WORKLOADS[0] if n is None else W.ragged_workload(n, 2)

@@ -23,8 +23,9 @@ from gpu_util import MEAN_ABS, SCALE, check, f64, oracle_rows_i8, problem_for, r
 
 pytestmark = pytest.mark.gpu
 
+# 384, 385, 769: at and past the edges of the int8 forward's 384-row query tiles
 SIZES = [(1, 1, False), (2, 2, True), (63, 1, False), (65, 2, False), (255, 1, True), (257, 3, False),
-         (1000, 2, True), (4099, 2, False), (20011, 2, True)]
+         (384, 1, False), (385, 2, True), (769, 2, False), (1000, 2, True), (4099, 2, False), (20011, 2, True)]
 
 
 @pytest.fixture(autouse=True)

@@ -304,10 +304,12 @@ def test_int8_codes_and_scales_bit_exact(cfg, n, h):
 
 def _scores_windows(n):
     """(row0, nrows, col0, ncols) windows: the sequence start, the end (the
-    ragged last query tile and key block), single elements and a window that
-    crosses several query tiles and key tiles."""
+    ragged last query tile and key block), single elements, a window that
+    crosses several query tiles and key tiles, and one across the first
+    384-row query tile edge."""
     w = [(0, min(n, 300), 0, min(n, 200)), (max(0, n - 70), min(70, n), max(0, n - 130), min(130, n)),
-         (n // 3, 1, n // 2, 1), (5, min(n - 5, 250), 3, min(n - 3, 333))]
+         (n // 3, 1, n // 2, 1), (5, min(n - 5, 250), 3, min(n - 3, 333)),
+         (360, min(60, n - 360), 0, min(n, 100))]
     return [x for x in w if x[1] >= 1 and x[3] >= 1]
 
 
@@ -323,7 +325,7 @@ def _check_scores(p8, q8, k8, heads, windows, layouts=(0, 1)):
                 assert np.array_equal(out.cpu().numpy().astype(np.int64), ref), (hh, r0, nr, c0, nc, lay)
 
 
-@pytest.mark.parametrize("cfg,n,h", [(0, None, None), (41, 4099, 2), (42, 129, 1), (43, 1, 1)])
+@pytest.mark.parametrize("cfg,n,h", [(0, None, None), (41, 4099, 2), (42, 129, 1), (43, 1, 1), (44, 385, 2)])
 def test_int8_scores_i32_bit_exact(cfg, n, h):
     # the int8 forward kernels' own Q'K'^T path (the bf16-V and the E4M3-V
     # forms' K' row orders) against exact integer products
@@ -333,7 +335,10 @@ def test_int8_scores_i32_bit_exact(cfg, n, h):
     _check_scores(p8, q8, k8, range(wl.heads), _scores_windows(wl.n_tokens))
 
 
-@pytest.mark.parametrize("cfg,n,h", [(0, None, None), (51, 1000, 2), (52, 65, 2), (53, 4099, 2)])
+# 383, 385, 769: either side of the int8 forward's 384-row query tiles (1000 and
+# 65 also take rows past N_pad in the last tile)
+@pytest.mark.parametrize("cfg,n,h", [(0, None, None), (51, 1000, 2), (52, 65, 2), (53, 4099, 2),
+                                     (54, 383, 2), (55, 385, 2), (56, 769, 1)])
 def test_int8_forward_matches_oracle(cfg, n, h):
     wl = W.WORKLOADS[0] if n is None else W.ragged_workload(n, h)
     inp = W.make_inputs(cfg, wl)
