@@ -45,8 +45,7 @@ int check_problem(const h3attn_problem* p) {
     int sum = 0;
     for (int a = 0; a < 3; ++a) {
         const int s = p->rope_sections[a];
-        if (s < 0) return H3ATTN_E_SHAPE;
-        if (s % 16) return H3ATTN_E_UNSUPPORTED;
+        if (s < 0 || s % 2) return H3ATTN_E_SHAPE;
         sum += s;
     }
     if (sum != p->head_dim) return H3ATTN_E_SHAPE;
@@ -270,6 +269,9 @@ int forward_common(const h3attn_problem* p, const void* q_prep, const void* k_pr
     const bool i8 = p->qk_format == H3ATTN_QK_I8_BLK64;
     if (rq) {
         if (i8 != rq->int8 || fp8v) return H3ATTN_E_UNSUPPORTED;
+        // the fused prologue pairs whole 8-element chunks only
+        if (!h3::sections_are_chunks(p->rope_sections[0], p->rope_sections[1], p->rope_sections[2]))
+            return H3ATTN_E_UNSUPPORTED;
         if ((rc = check_in_view(rq->q, rq->st, rq->sh))) return rc;
         if ((rc = check_in_view(rq->gamma, 0, rq->g_sh))) return rc;
         if (!rq->pos) return H3ATTN_E_NULL;

@@ -60,6 +60,10 @@ hipError_t launch_prep_ksmooth(const PrepParams& P, hipStream_t stream);
 hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t stream);
 // query rows per work-group of that forward (FwdParams::qtiles counts tiles of this size)
 int forward_tile_rows(bool int8);
+// RoPE section widths that are multiples of 16: each lane's 8-element chunk of a
+// first half pairs with one whole chunk of the second half (the fast prep form,
+// and the only one the fused-Q forwards build)
+inline bool sections_are_chunks(int s0, int s1, int s2) { return s0 % 16 == 0 && s1 % 16 == 0 && s2 % 16 == 0; }
 // bf16 Q'/K', V through its view, Q' computed from raw Q in the prologue
 hipError_t launch_forward_fused_q(const FwdParams& P, bool int8, hipStream_t stream);
 hipError_t launch_prep_v(const PrepVParams& P, hipStream_t stream);

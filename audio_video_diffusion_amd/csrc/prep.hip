@@ -22,6 +22,16 @@
 // With K smoothing (the K-mean step of the same quantised path) the per-head,
 // per-channel mean of K' is subtracted before K is quantised, in three passes
 // (see PrepMode).
+//
+// Section widths that are even but not multiples of 16 (kGen) split chunks
+// between section halves, so a lane's partner elements lie in other lanes'
+// chunks.  Then each eight-lane group passes its row through LDS: the lanes
+// load chunks p and p + 8 as usual and store them there, each lane gathers
+// the 8 first-half elements of its generic slot (gen_slot_of) and their
+// partners, normalises and rotates them with the same routine, scatters the
+// bf16 results back, and reads chunks p and p + 8 of the result; from there
+// on (stores, quantisation, K sums) the kernel runs as with chunk slots
+// a = p, b = p + 8.
 #include "common.h"
 #include "params.h"
 #include "rope_norm.h"
@@ -39,7 +49,7 @@ namespace h3 {
 // forwards that compute Q' in their prologue).
 enum PrepMode { kPrepBf16 = 0, kPrepI8 = 1, kPrepI8Sums = 2, kPrepI8Smooth = 3, kPrepBf16K = 4, kPrepI8K = 5 };
 
-template <int kMode>
+template <int kMode, bool kGen = false>
 __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
     constexpr bool kInt8 = kMode == kPrepI8 || kMode == kPrepI8Sums || kMode == kPrepI8Smooth || kMode == kPrepI8K;
     // Q' produced in this pass
@@ -49,31 +59,98 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
     const int row = tid >> 3;            // 0..31
     const int p = tid & 7;               // slot
     const int t0 = blockIdx.x * 64;
-    const Slot sl = slot_of(p, P.sec0, P.sec1, P.sec2);
+    const Slot sl = kGen ? Slot{p, p + 8, 0, 0, 0} : slot_of(p, P.sec0, P.sec1, P.sec2);
+    const GenSlot gs = gen_slot_of(p, P.sec0, P.sec1, P.sec2);     // kGen only
 
     int tok[2];
     bool valid[2];
     float cs[2][8], sn[2][8];
     double freq[8];
-    rope_freqs(sl, P.rho0, P.rho1, P.rho2, freq);
+    if constexpr (kGen)
+        rope_freqs_gen(gs, P.rho0, P.rho1, P.rho2, freq);
+    else
+        rope_freqs(sl, P.rho0, P.rho1, P.rho2, freq);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         tok[t] = t0 + row + 32 * t;
         valid[t] = tok[t] < P.n;
-        const double pv = valid[t] ? (double)P.pos[(int64_t)tok[t] * 3 + sl.axis] : 0.0;
-        rope_angles(pv, freq, cs[t], sn[t]);
+        if constexpr (kGen) {
+            double pv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pv[i] = valid[t] ? (double)P.pos[(int64_t)tok[t] * 3 + gs.ax[i]] : 0.0;
+            rope_angles_t<true>(pv, freq, cs[t], sn[t]);
+        } else {
+            const double pv = valid[t] ? (double)P.pos[(int64_t)tok[t] * 3 + sl.axis] : 0.0;
+            rope_angles(pv, freq, cs[t], sn[t]);
+        }
     }
 
+    // gamma of the slot's elements: chunks a and b, or (kGen) the generic
+    // slot's first-half elements and their partners
     float gqa[8], gqb[8], gka[8], gkb[8];
     auto load_gamma = [&](int h) {
-        if constexpr (kDoQ) {            // gamma_q is absent (NULL) when Q' is not produced
-            unpack8(ld16(P.gq + h * P.g_sh + 8 * sl.a), gqa);
-            unpack8(ld16(P.gq + h * P.g_sh + 8 * sl.b), gqb);
+        if constexpr (kGen) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if constexpr (kDoQ) {
+                    gqa[i] = bf16_to_f32(P.gq[h * P.g_sh + gs.e1[i]]);
+                    gqb[i] = bf16_to_f32(P.gq[h * P.g_sh + gs.e2[i]]);
+                }
+                gka[i] = bf16_to_f32(P.gk[h * P.g_sh + gs.e1[i]]);
+                gkb[i] = bf16_to_f32(P.gk[h * P.g_sh + gs.e2[i]]);
+            }
+        } else {
+            if constexpr (kDoQ) {        // gamma_q is absent (NULL) when Q' is not produced
+                unpack8(ld16(P.gq + h * P.g_sh + 8 * sl.a), gqa);
+                unpack8(ld16(P.gq + h * P.g_sh + 8 * sl.b), gqb);
+            }
+            unpack8(ld16(P.gk + h * P.g_sh + 8 * sl.a), gka);
+            unpack8(ld16(P.gk + h * P.g_sh + 8 * sl.b), gkb);
         }
-        unpack8(ld16(P.gk + h * P.g_sh + 8 * sl.a), gka);
-        unpack8(ld16(P.gk + h * P.g_sh + 8 * sl.b), gkb);
     };
     load_gamma(0);
+
+    // kGen: the row of this eight-lane group (bf16 bits), for the gather and
+    // scatter; the lanes of a group are one wave's, whose LDS accesses run in
+    // program order (the waits below also order them for the compiler)
+    __shared__ uint16_t grow[kGen ? 32 : 1][kGen ? kHeadDim : 1];
+    auto rot = [&](u32x4 ca, u32x4 cb, const float* ga, const float* gb, const float* c8, const float* s8,
+                   u32x4& oa, u32x4& ob, float* ra, float* rb) {
+        if constexpr (kGen) {
+            uint16_t* rw = grow[row];
+            *reinterpret_cast<u32x4*>(rw + 8 * sl.a) = ca;
+            *reinterpret_cast<u32x4*>(rw + 8 * sl.b) = cb;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            float xa[8], xb[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                xa[i] = bf16_to_f32(rw[gs.e1[i]]);
+                xb[i] = bf16_to_f32(rw[gs.e2[i]]);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            u32x4 ga4, gb4;
+            float fa[8], fb[8];
+            norm_rotate(xa, xb, ga, gb, c8, s8, P.eps, ga4, gb4, fa, fb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                rw[gs.e1[2 * i]] = (uint16_t)(ga4[i] & 0xffff);
+                rw[gs.e1[2 * i + 1]] = (uint16_t)(ga4[i] >> 16);
+                rw[gs.e2[2 * i]] = (uint16_t)(gb4[i] & 0xffff);
+                rw[gs.e2[2 * i + 1]] = (uint16_t)(gb4[i] >> 16);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            oa = *reinterpret_cast<const u32x4*>(rw + 8 * sl.a);
+            ob = *reinterpret_cast<const u32x4*>(rw + 8 * sl.b);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            unpack8(oa, ra);
+            unpack8(ob, rb);
+        } else {
+            float xa[8], xb[8];
+            unpack8(ca, xa);
+            unpack8(cb, xb);
+            norm_rotate(xa, xb, ga, gb, c8, s8, P.eps, oa, ob, ra, rb);
+        }
+    };
 
     __shared__ float red[2][2][4];      // [head parity][q/k][wave]
     // K smoothing, first pass: one head's bf16 K' block as fp32, [token][channel]
@@ -104,19 +181,14 @@ __global__ void __launch_bounds__(256) prep_kernel(PrepParams P) {
         u32x4 oqa[2], oqb[2], oka[2], okb[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            float xa[8], xb[8];
             if constexpr (kDoQ) {
-                unpack8(qa[t], xa);
-                unpack8(qb[t], xb);
-                norm_rotate(xa, xb, gqa, gqb, cs[t], sn[t], P.eps, oqa[t], oqb[t], rq[t], rq[t] + 8);
+                rot(qa[t], qb[t], gqa, gqb, cs[t], sn[t], oqa[t], oqb[t], rq[t], rq[t] + 8);
             } else {
                 oqa[t] = oqb[t] = u32x4{0, 0, 0, 0};
 #pragma unroll
                 for (int i = 0; i < 16; ++i) rq[t][i] = 0.f;
             }
-            unpack8(ka[t], xa);
-            unpack8(kb[t], xb);
-            norm_rotate(xa, xb, gka, gkb, cs[t], sn[t], P.eps, oka[t], okb[t], rk[t], rk[t] + 8);
+            rot(ka[t], kb[t], gka, gkb, cs[t], sn[t], oka[t], okb[t], rk[t], rk[t] + 8);
             if (!valid[t]) {
                 oqa[t] = oqb[t] = oka[t] = okb[t] = u32x4{0, 0, 0, 0};
 #pragma unroll
@@ -244,32 +316,43 @@ __global__ void __launch_bounds__(256) ksum_reduce(const float* sums, float* mea
     mean[i] = acc / (float)n;       // IEEE division (the library is compiled without fast-math)
 }
 
+// one prep pass in the chunk-slot form, or the generic one when a section
+// width is not a multiple of 16
+template <int kMode>
+void launch_mode(const PrepParams& P, dim3 grid, hipStream_t stream) {
+    if (sections_are_chunks(P.sec0, P.sec1, P.sec2))
+        hipLaunchKernelGGL((prep_kernel<kMode, false>), grid, dim3(256), 0, stream, P);
+    else
+        hipLaunchKernelGGL((prep_kernel<kMode, true>), grid, dim3(256), 0, stream, P);
+}
+
 hipError_t launch_prep(const PrepParams& P, bool int8, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
-    dim3 grid(P.npad / 64), block(256);
+    const dim3 grid(P.npad / 64);
     if (int8)
-        hipLaunchKernelGGL(prep_kernel<kPrepI8>, grid, block, 0, stream, P);
+        launch_mode<kPrepI8>(P, grid, stream);
     else
-        hipLaunchKernelGGL(prep_kernel<kPrepBf16>, grid, block, 0, stream, P);
+        launch_mode<kPrepBf16>(P, grid, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_prep_k(const PrepParams& P, bool int8, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
+    const dim3 grid(P.npad / 64);
     if (int8)
-        hipLaunchKernelGGL(prep_kernel<kPrepI8K>, dim3(P.npad / 64), dim3(256), 0, stream, P);
+        launch_mode<kPrepI8K>(P, grid, stream);
     else
-        hipLaunchKernelGGL(prep_kernel<kPrepBf16K>, dim3(P.npad / 64), dim3(256), 0, stream, P);
+        launch_mode<kPrepBf16K>(P, grid, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_prep_ksmooth(const PrepParams& P, hipStream_t stream) {
     (void)hipGetLastError();     // clear an error left by an earlier, unrelated call
-    dim3 grid(P.npad / 64), block(256);
-    hipLaunchKernelGGL(prep_kernel<kPrepI8Sums>, grid, block, 0, stream, P);
+    const dim3 grid(P.npad / 64), block(256);
+    launch_mode<kPrepI8Sums>(P, grid, stream);
     hipLaunchKernelGGL(ksum_reduce, dim3((P.h * kHeadDim + 255) / 256), block, 0, stream,
                        static_cast<const float*>(P.k_out), P.k_mean, P.h, P.nblk, P.n);
-    hipLaunchKernelGGL(prep_kernel<kPrepI8Smooth>, grid, block, 0, stream, P);
+    launch_mode<kPrepI8Smooth>(P, grid, stream);
     return hipGetLastError();
 }
 

@@ -39,6 +39,33 @@ __device__ __forceinline__ Slot slot_of(int p, int s0, int s1, int s2) {
     return r;
 }
 
+// Any even section widths (the prep only): slot p takes the first-half
+// elements k = 8p .. 8p+7 of the 64 that the three sections' first halves hold
+// in order (t, then h, then w), and their partners.  Element i of the slot is
+// head-dim index e1[i], angle index j[i] of section ax[i]; its partner is
+// e1[i] + s/2.
+struct GenSlot {
+    int e1[8], e2[8], ax[8], j[8];
+};
+
+__device__ __forceinline__ GenSlot gen_slot_of(int p, int s0, int s1, int s2) {
+    GenSlot g;
+    const int h0 = s0 / 2, h1 = s1 / 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int k = 8 * p + i;
+        const int ax = k < h0 ? 0 : k < h0 + h1 ? 1 : 2;
+        const int j = ax == 0 ? k : ax == 1 ? k - h0 : k - h0 - h1;
+        const int off = ax == 0 ? 0 : ax == 1 ? s0 : s0 + s1;
+        const int half = (ax == 0 ? s0 : ax == 1 ? s1 : s2) / 2;
+        g.e1[i] = off + j;
+        g.e2[i] = off + j + half;
+        g.ax[i] = ax;
+        g.j[i] = j;
+    }
+    return g;
+}
+
 __device__ __forceinline__ void unpack8(u32x4 v, float* f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -124,6 +151,23 @@ __device__ __forceinline__ void rope_freqs(const Slot& sl, double rho0, double r
     for (int i = 1; i < 8; ++i) f[i] = f[i - 1] * rho;
 }
 
+// The generic slot's 8 inverse frequencies theta^(-2j/s): rho^j of each
+// element's own section by binary powering.
+__device__ __forceinline__ void rope_freqs_gen(const GenSlot& g, double rho0, double rho1, double rho2, double* f) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const double rho = g.ax[i] == 0 ? rho0 : g.ax[i] == 1 ? rho1 : rho2;
+        double acc = 1.0, b = rho;
+#pragma unroll
+        for (int bit = 0; bit < 6; ++bit) {        // j < 64
+            if ((g.j[i] >> bit) & 1) acc = acc * b;
+            b = b * b;
+        }
+        f[i] = acc;
+    }
+}
+
 // cos/sin of the angles phi = pos * f[i].  phi is formed and reduced in fp64
 // (with positions in the thousands an fp32 product alone is off by ~1e-4
 // rad): k = rint(phi * 2/pi), r = phi - k pi/2 with one fused multiply-add,
@@ -131,11 +175,14 @@ __device__ __forceinline__ void rope_freqs(const Slot& sl, double rho0, double r
 // fp32 and sin r, cos r come from their Taylor series through r^9 and r^10
 // (truncation below 2e-9 on |r| <= pi/4, under fp32 rounding), evaluated by
 // Horner's rule, and the quadrant k mod 4 swaps and negates them.
-__device__ __forceinline__ void rope_angles(double pv, const double* f, float* cs, float* sn) {
+// kPerElement: pv holds one position per element (the generic slots, whose
+// elements may belong to different sections).
+template <bool kPerElement = false>
+__device__ __forceinline__ void rope_angles_t(const double* pv, const double* f, float* cs, float* sn) {
 #pragma clang fp contract(off)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const double phi = pv * f[i];
+        const double phi = pv[kPerElement ? i : 0] * f[i];
         const double k = rint(phi * 0.636619772367581343076);                 // 2 / pi
         const float r = (float)__builtin_fma(-k, 1.57079632679489661923, phi); // pi / 2
         const int q = (int)__builtin_fma(-4.0, floor(k * 0.25), k);           // k mod 4, exact
@@ -158,6 +205,9 @@ __device__ __forceinline__ void rope_angles(double pv, const double* f, float* c
         sn[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, odd ? c : s) ^ neg_s);
         cs[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, odd ? s : c) ^ neg_c);
     }
+}
+__device__ __forceinline__ void rope_angles(double pv, const double* f, float* cs, float* sn) {
+    rope_angles_t<false>(&pv, f, cs, sn);
 }
 
 // The int8 code of each of v[0..3] at reciprocal scale inv (round to nearest

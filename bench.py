@@ -62,7 +62,10 @@ PEAK_HBM_GBS = 8000.0
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
     "kernel": "h3attn_forward_fused_q",
-    "source_sha256": "9c7b9f105179e2c7acbe6ca0c21161b715270b57572416db9e50dba682155a05",
+    # sources as profiled were 9c7b9f105179e2c7...; the later sources add the
+    # prep's generic-section helpers to rope_norm.h, and the forward's gfx950
+    # instructions are identical
+    "source_sha256": "a72f768e34adcf4558263e61d445ae26cce27cfa1f519e448311ce512bf30de6",
     # the copy's kernel reads 524,319 KiB per 1 GiB as FETCH_SIZE (factor 2.0) and
     # writes 1,048,576 KiB as WRITE_SIZE (factor 1.0)
     "fetch_kib": 13350854.3, "fetch_scale": 2.0,

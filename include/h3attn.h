@@ -58,7 +58,8 @@ typedef enum {
     H3ATTN_OK = 0,
     H3ATTN_E_NULL = -1,         /* a required pointer is NULL                         */
     H3ATTN_E_SHAPE = -2,        /* bad N/H/sections/strides/window/scale value         */
-    H3ATTN_E_UNSUPPORTED = -3,  /* head_dim != 128, unknown format, sections not /16, V token stride > 2^24 */
+    H3ATTN_E_UNSUPPORTED = -3,  /* head_dim != 128, unknown format, V token stride > 2^24,
+                                   fused-Q forward with sections not /16              */
     H3ATTN_E_ALIGN = -4,        /* pointer not 16-byte aligned or stride not /8 (/16) */
     H3ATTN_E_ALIAS = -5,        /* an output byte range overlaps another buffer        */
     H3ATTN_E_HIP = -6           /* the HIP runtime reported an error on launch         */
@@ -76,14 +77,17 @@ typedef struct {
     int32_t n_heads;            /* H >= 1                                               */
     int32_t head_dim;           /* d: must be 128                                       */
     int32_t rope_sections[3];   /* widths of the t, h, w slices of d, in this order:
-                                   contiguous [0,s0), [s0,s0+s1), [s0+s1,d); each >= 0,
-                                   a multiple of 16, summing to d (e.g. 32, 48, 48).
-                                   Split-half RoPE pairs element j of a section's first
-                                   half with j of its second half; the kernels give each
-                                   lane an 8-element chunk of a first half and its
-                                   partner chunk, so halves must be whole chunks: an
-                                   even width that is not a multiple of 16 returns
-                                   H3ATTN_E_UNSUPPORTED (no cross-lane pairing is built) */
+                                   contiguous [0,s0), [s0,s0+s1), [s0+s1,d); each even
+                                   and >= 0, summing to d (e.g. 32, 48, 48); E_SHAPE
+                                   otherwise.  Split-half RoPE pairs element j of a
+                                   section's first half with j of its second half.
+                                   With every width a multiple of 16 each lane's
+                                   8-element chunk of a first half pairs with a whole
+                                   chunk of the second half (the fast form); other
+                                   even widths take a prep form that pairs elements
+                                   through LDS (slower, same arithmetic per element),
+                                   and the fused-Q forwards, which build only the chunk
+                                   form, return H3ATTN_E_UNSUPPORTED for them          */
     float rope_theta;           /* RoPE base, > 0 (e.g. 10000)                          */
     float rms_eps;              /* RMSNorm epsilon, >= 0 (e.g. 1e-6)                    */
     int32_t qk_format;          /* h3attn_qk_format                                     */
@@ -300,7 +304,8 @@ int h3attn_prep_k(const h3attn_problem* p,
  *            the (t, h, w) positions).
  * k_prep:    bf16 K' from h3attn_prep_k (or h3attn_prep) for the same descriptor.
  * v, o, softmax_scale: as for h3attn_forward; o must not overlap any input.
- * Requires qk_format == H3ATTN_QK_BF16 (E_UNSUPPORTED otherwise).
+ * Requires qk_format == H3ATTN_QK_BF16 and RoPE section widths that are
+ * multiples of 16 (E_UNSUPPORTED otherwise).
  * Errors: as for h3attn_prep.
  */
 int h3attn_forward_fused_q(const h3attn_problem* p,
@@ -342,7 +347,8 @@ int h3attn_prep_k_i8(const h3attn_problem* p,
  *            descriptor.
  * v, o, softmax_scale: as for h3attn_forward (bf16 V view); o must not
  *            overlap any input.
- * Requires qk_format == H3ATTN_QK_I8_BLK64 (E_UNSUPPORTED otherwise).
+ * Requires qk_format == H3ATTN_QK_I8_BLK64 and RoPE section widths that are
+ * multiples of 16 (E_UNSUPPORTED otherwise).
  * Errors: as for h3attn_prep.
  */
 int h3attn_forward_fused_q_i8(const h3attn_problem* p,

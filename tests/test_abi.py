@@ -102,10 +102,17 @@ def test_size_limits():
 def test_section_validation():
     p = A.problem(1000, 3, sections=(32, 48, 32))
     assert prep(p) == -2                       # does not sum to 128
-    p = A.problem(1000, 3, sections=(40, 40, 48))
-    assert prep(p) == -3                       # not multiples of 16
+    # any even widths pass the descriptor check (the null Q pointer is what fails)
+    for sec in ((40, 40, 48), (34, 46, 48), (2, 62, 64), (0, 64, 64), (128, 0, 0)):
+        assert prep(A.problem(1000, 3, sections=sec), q=None) == -1, sec
+        assert fwd(A.problem(1000, 3, sections=sec), q=None) == -1, sec
+    p = A.problem(1000, 3, sections=(33, 47, 48))
+    assert prep(p) == -2                       # odd widths
     p = A.problem(1000, 3, sections=(-16, 96, 48))
     assert prep(p) == -2
+    # the fused-Q forwards build only whole-chunk pairs
+    assert fwd_fq(A.problem(1000, 3, sections=(40, 40, 48))) == -3
+    assert fwd_fq8(A.problem(1000, 3, A.QK_I8_BLK64, sections=(40, 40, 48)), ks=None) == -3
     assert prep(A.problem(1000, 3, theta=0.0)) == -2
     assert prep(A.problem(1000, 3, eps=-1.0)) == -2
     assert prep(A.problem(1000, 3, eps=float("nan"))) == -2
