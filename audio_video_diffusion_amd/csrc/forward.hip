@@ -12,9 +12,8 @@
 //   owns one 32-row block and keeps its Q' rows in registers.  Waves w and
 //   w+4 share a SIMD: per wave the state is small (O^T in 64 AGPRs), so two
 //   waves fit each SIMD's register file and the hardware overlaps one wave's
-//   softmax with the other's matrix-core work.  The int8 forms that read Q'
-//   from the prep run twelve waves and 384 rows instead, three waves per
-//   SIMD (see kW);
+//   softmax with the other's matrix-core work.  The int8 forms run twelve
+//   waves and 384 rows instead, three waves per SIMD (see kW);
 // * the work-group streams K'/V in tiles of 64 keys through four LDS stages,
 //   fetched three tiles ahead with buffer -> LDS DMA (buffer_load_dwordx4 ...
 //   lds: 1 KB per wave instruction, no registers in between; waves 0..7 each
@@ -317,8 +316,8 @@ constexpr float kPLog2Fp8 = 0.8f;
 // Q'K'^T chain then starts from -m, so the scores leave the matrix core ready
 // for exp2.  Int8 format: rounded to bf16 and quantised per 64-row block
 // exactly as the prep does (codes and scales identical), then the int8 path.
-// kW = 12 (int8 Q'/K' read from the prep, bf16 or E4M3 V): twelve waves, three
-// per SIMD, own 384 query rows.  The int8 state is small enough (Q' codes in
+// kW = 12 (int8 Q'/K', bf16 or E4M3 V, Q' from the prep or fused): twelve
+// waves, three per SIMD, own 384 query rows.  The int8 state is small enough (Q' codes in
 // 16 registers, K' operands half the bf16 size) for three waves in a SIMD's
 // register file, 168 registers each; the K'/V stream then serves 384 queries
 // instead of 256 (a third fewer L2 -> LDS bytes per FLOP) and each SIMD has a
