@@ -27,7 +27,7 @@ SYNC_LIB_PATH = os.path.join(PKG, "libh3attn_sync.so")
 
 QK_BF16 = 0
 QK_I8_BLK64 = 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_UNSUPPORTED", -4: "E_ALIGN",
           -5: "E_ALIAS", -6: "E_HIP"}

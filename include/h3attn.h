@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define H3ATTN_ABI_VERSION 7
+#define H3ATTN_ABI_VERSION 8
 
 typedef enum {
     H3ATTN_OK = 0,

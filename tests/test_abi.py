@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(path):
 
 
 def test_abi_version_and_status_strings():
-    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 7
+    assert A.lib.h3attn_abi_version() == A.ABI_VERSION == 8
     for s in (0, -1, -2, -3, -4, -5, -6, 7):
         assert A.lib.h3attn_status_string(s)
 
