@@ -62,14 +62,11 @@ PEAK_HBM_GBS = 8000.0
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
     "kernel": "h3attn_forward_fused_q",
-    # sources as profiled were 9c7b9f105179e2c7...; the later sources add the
-    # prep's generic-section helpers to rope_norm.h and change comments, and
-    # the forward's gfx950 instructions are identical
     "source_sha256": "6e79c4ebb6a8e5d9e6be93b9ef42db1bcc97f9abb38149c555a11ca7f2209f9a",
     # the copy's kernel reads 524,319 KiB per 1 GiB as FETCH_SIZE (factor 2.0) and
     # writes 1,048,576 KiB as WRITE_SIZE (factor 1.0)
-    "fetch_kib": 13350854.3, "fetch_scale": 2.0,
-    "write_kib": 820275.2, "write_scale": 1.0,
+    "fetch_kib": 13350855.0, "fetch_scale": 2.0,
+    "write_kib": 817599.6, "write_scale": 1.0,
 }
 
 
