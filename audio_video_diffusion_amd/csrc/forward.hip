@@ -145,18 +145,20 @@ __device__ __forceinline__ void dma16_buf_so(const u32x4& rsrc, uint32_t voff, u
 // stays in AGPRs: these MFMAs are issued as inline asm to pin the register
 // classes.  The first of a chain writes an early-clobber destination (it must
 // not overlap the A/B operands); the rest accumulate in place.
-// A matrix-core product reads a VGPR two wait states after a VALU write of it
-// at the earliest (the compiler pads its own products so on gfx950), but it
-// cannot see a product inside asm: the chain's first product, whose operands
-// (the start value above all) the compiler may materialise with VALU moves
-// just before it, therefore starts with s_nop 1.  The later products of a
-// chain read the previous product's result (forwarded) and operands loaded
-// from LDS.
+// A matrix-core product reads a register two wait states after a VALU write of
+// it at the earliest (the compiler pads its own products so on gfx950), but it
+// cannot see a product inside asm, and where it places the VALU moves that
+// feed one (a start value, a Q' operand copied into an AGPR) depends on its
+// register allocation: a build with another scheduler option put such a copy
+// right before a product of the fused int8 chain and changed its results.
+// Every asm product therefore starts with s_nop 1 (same process and box, all
+// forms within +-0.2% except bf16 Q'/K' with E4M3 V, 1.3% faster; outputs
+// bit-identical).
 __device__ __forceinline__ void mfma_s(f32x16& d, const bf16x8& a, const bf16x8& b, bool first) {
     if (first)
         asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
     else
-        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+        asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
 // The chain's first product of the fused-Q form: it adds to c0, which holds
@@ -174,7 +176,7 @@ __device__ __forceinline__ void mfma_s_i8(i32x16& d, const i32x4& a, const i32x4
     if (first)
         asm("s_nop 1\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "a"(b), "v"(c0));
     else
-        asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+        asm("s_nop 1\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
 // Tile-local key of accumulator element e of block kb for lane half hh.
