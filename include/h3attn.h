@@ -336,7 +336,7 @@ int h3attn_prep_k_i8(const h3attn_problem* p,
  * h3attn_forward_fused_q_i8 - h3attn_forward in the int8 format with the Q
  * half of h3attn_prep moved into the forward (the entry fusion of the
  * quantised path, "H3 Runtime Current State", Owned Performance Kernels: the
- * fused entry kernel; Q quantization): each work-group computes its 256 Q' rows
+ * fused entry kernel; Q quantization): each work-group computes its 384 Q' rows
  * from raw Q with the prep's arithmetic, rounds them to bf16, and quantises
  * each 64-row block with the prep's absmax, scale and rounding, so its codes
  * and scales are those h3attn_prep would write, and the output is that of
