@@ -347,18 +347,23 @@ fwd8_kernel(FwdParams P) {
     constexpr int kKTileB = kBN * D::kRowB;        // 16 KB (bf16) or 8 KB (int8)
     constexpr int kVTileB = kBN * (kFp8V ? 128 : 256);   // 8 KB (E4M3) or 16 KB (bf16)
     constexpr int kDma8 = D::kN + (kScores ? 0 : D::kNV);   // DMA instructions per wave per tile
-    // Staggered barrier (bf16 Q'/K' with E4M3 V only): waves 4..7 take the
-    // per-tile barrier between their softmax and their P V product instead of
-    // after it, so after each barrier they run P V of tile j while waves 0..3
-    // start Q'K'^T of tile j + 1: the two waves of each SIMD stay half a tile
-    // apart.  Each row's arithmetic is unchanged (outputs bit-identical).  A
-    // lagging wave still reads V of tile j after the barrier that ends tile j,
-    // so the stage of tile j may only be refilled after the next barrier:
-    // tiles are fetched two ahead instead of three.  Same process and box,
-    // 129,410 tokens: bf16 Q'/K' with E4M3 V -2.8%; the bf16-V forms were
-    // slower this way (bf16 +5.1%, fused Q prep +4.0%, int8 Q'/K' +1.2%) and
-    // keep the common barrier.
-    constexpr bool kStagger = kW == 8 && kFp8V && !kInt8 && !kScores;
+    // Staggered barrier (the eight-wave bf16 Q'/K' forms with Q' from the
+    // prep): waves 4..7 take the per-tile barrier between their softmax and
+    // their P V product instead of after it, so after each barrier they run
+    // P V of tile j while waves 0..3 start Q'K'^T of tile j + 1: the two waves
+    // of each SIMD stay half a tile apart.  Each row's arithmetic is unchanged
+    // (outputs bit-identical).  A lagging wave still reads V of tile j after
+    // the barrier that ends tile j, so the stage of tile j may only be
+    // refilled after the next barrier: tiles are fetched two ahead instead of
+    // three.  The SIMD's issue arbiter favours the older wave (0..3), which
+    // starved the lagging wave's P V behind the other's Q'K'^T chain; with
+    // bf16 V the lagging wave runs its P V at raised issue priority.  Same
+    // process and box, 129,410 tokens, against the common barrier: bf16 Q'/K'
+    // with E4M3 V -2.8% (the raised priority made it +5.5%), bf16 Q'/K' and V
+    // -1.5 to -2.2% (+2.9% without the raised priority); the fused-Q form was
+    // level with it (+0.4 to -0.5%) and keeps the common barrier, as do the
+    // twelve-wave int8 forms.
+    constexpr bool kStagger = kW == 8 && !kInt8 && !kScores && !kFuseQ;
     // tiles fetched ahead of the one being computed
     constexpr int kAhead = kStagger ? 2 : 3;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * (kKTileB + kVTileB)];
@@ -745,7 +750,10 @@ fwd8_kernel(FwdParams P) {
                         }
                     }
                 l += t;
-                if (behind) tile_sync();
+                if (behind) {
+                    tile_sync();
+                    __builtin_amdgcn_s_setprio(2);     // the lagging wave's P V (kStagger)
+                }
                 // O^T += V^T P^T
                 const uint8_t* vb_ = vbuf_st(st);
                 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -767,6 +775,10 @@ fwd8_kernel(FwdParams P) {
                         for (int cc = 0; cc < 4; ++cc)
                             O[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cc], Pb[kb][s], O[cc], 0, 0, 0);
                     }
+                if (behind) {
+                    __builtin_amdgcn_sched_barrier(0);   // every product issued first
+                    __builtin_amdgcn_s_setprio(0);
+                }
             }
         }
         if (!behind) tile_sync();

@@ -62,11 +62,11 @@ PEAK_HBM_GBS = 8000.0
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
     "kernel": "h3attn_forward_fused_q",
-    "source_sha256": "a4fa63ccf03768082a9411273c2a1a45692725c078a0bd31bf9505502d8a6b74",
+    "source_sha256": "6dca3c60e868ef0ffe0a2c24dcbecd3d0bc2e54e81e765961121bad079685509",
     # the copy's kernel reads 524,319 KiB per 1 GiB as FETCH_SIZE (factor 2.0) and
     # writes 1,048,576 KiB as WRITE_SIZE (factor 1.0)
-    "fetch_kib": 13350848.2, "fetch_scale": 2.0,
-    "write_kib": 816351.1, "write_scale": 1.0,
+    "fetch_kib": 13350854.8, "fetch_scale": 2.0,
+    "write_kib": 817485.8, "write_scale": 1.0,
 }
 
 
