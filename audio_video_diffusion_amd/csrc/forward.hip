@@ -19,7 +19,8 @@
 //   lds: 1 KB per wave instruction, no registers in between; waves 0..7 each
 //   move 8 of the 64 rows).  K' rows land permuted, V rows stay row-major; 16-byte
 //   chunks are XOR-swizzled so the operand reads hit every LDS bank.  One
-//   barrier per tile;
+//   barrier per tile (the separate-prep eight-wave forms stagger it between
+//   the two waves of a SIMD and fetch two tiles ahead: kStagger);
 // * everything is computed transposed so that one lane owns one query column:
 //     S^T (keys x queries) = K' Q'^T     with v_mfma_f32_32x32x16_bf16
 //                                        (int8: v_mfma_i32_32x32x32_i8)
@@ -33,7 +34,9 @@
 //   (lane half h holds rows 8i+4h+j) directly yields, per lane, 8 consecutive
 //   keys for each 16-key step of the P V product: P needs no lane movement;
 // * online softmax in base 2: one fp32 FMA per score applies scale*log2(e)
-//   (times s_q*s_k in int8 mode) and subtracts the running max m, then exp2.
+//   (times s_q*s_k in int8 mode) and subtracts the running max m, then exp2
+//   (the fused bf16 form carries the scale in Q' and starts each Q'K'^T
+//   chain from -m, so its scores go to exp2 as they are).
 //   The running max is only raised when it grows by more than 2^8 (exact: the
 //   stale max cancels between numerator and denominator, P stays <= 256).  The
 //   row sum adds the bf16-rounded P that the P V product uses, two at a time

@@ -94,3 +94,24 @@ def test_clock_sampler_reads_the_starred_level(tmp_path):
     with c2:
         pass
     assert c2.summary() is None
+
+
+def test_code_hash_ignores_comments_only(tmp_path, monkeypatch):
+    src = os.path.join(bench.ROOT, "audio_video_diffusion_amd", "csrc")
+    dst = tmp_path / "audio_video_diffusion_amd" / "csrc"
+    dst.mkdir(parents=True)
+    texts = {n: open(os.path.join(src, n), encoding="utf-8").read() for n in ("forward.hip", "rope_norm.h")}
+    base = bench.kernel_sources_sha256()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+
+    def digest(fwd):
+        (dst / "forward.hip").write_text(fwd, encoding="utf-8")
+        (dst / "rope_norm.h").write_text(texts["rope_norm.h"], encoding="utf-8")
+        return bench.kernel_sources_sha256()
+
+    assert digest(texts["forward.hip"]) == base
+    # comments and line breaks added: same code, same digest
+    assert digest("// a note\n" + texts["forward.hip"].replace("\n", "\n\n", 3) + "\n/* end */\n") == base
+    # a changed constant: another digest
+    assert "kRescaleLog2 = 8.0f" in texts["forward.hip"]
+    assert digest(texts["forward.hip"].replace("kRescaleLog2 = 8.0f", "kRescaleLog2 = 7.0f")) != base
