@@ -538,8 +538,14 @@ fwd8_kernel(FwdParams P) {
         __syncthreads();
     };
     const bool behind = kStagger && wave >= 4;
+    // bf16 Q'/K' with E4M3 V issues a tile's copies after its Q'K'^T chain,
+    // while the products run (same process and box, both orders: -1.1% and
+    // -1.4%); the bf16-V forms were slower so (+0.7 to +1.3%), and the int8
+    // forms spill.  Either way the copies refill the stage of tile j - 1
+    // (j - 2 when staggered), which every wave has left at the last barrier.
+    constexpr bool kLateFetch = kFp8V && !kInt8;
     auto tile = [&](int j, bool masked, int st) {
-        fetch(j + kAhead);
+        if constexpr (!kLateFetch) fetch(j + kAhead);
         debug_stage_sync();
         // S^T of this wave's 32 queries: S[kb] = LDS rows 32kb..32kb+31
         f32x16 S[2];
@@ -588,6 +594,7 @@ fwd8_kernel(FwdParams P) {
                     mfma_s(S[1], a[1][t], q[t], t == 0);
                 }
             }
+            if constexpr (kLateFetch) fetch(j + kAhead);
             asm volatile("s_nop 7\n\ts_nop 4" : "+v"(S[0]), "+v"(S[1]));      // as above
             debug_stage_sync();
         }
