@@ -16,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libh3attn.so")
 # race-detection build of the same sources (tests only)
 SYNC_LIB = os.path.join(PKG, "libh3attn_sync.so")
+# phase-timing build of the same sources (a measurement aid: include/h3attn_phase_timing.h)
+TIMING_LIB = os.path.join(PKG, "libh3attn_timing.so")
 SOURCES = ("api.hip", "prep.hip", "prep_v.hip", "forward.hip", "calib.hip")
 ARCH = "gfx950"
 
@@ -60,9 +62,11 @@ def _compile(out: str, defines=(), verbose: bool = False, asm: bool = False) -> 
 def build(verbose: bool = False, asm: bool = False) -> str:
     """Compile every HIP source into the in-tree shared library, and the same
     sources again into the race-detection build (a barrier after every LDS
-    stage of the forward, used by the tests only); returns the library path."""
+    stage of the forward, used by the tests only) and the phase-timing build
+    (shader-clock stamps in the forward's tile loop); returns the library path."""
     _compile(LIB, verbose=verbose, asm=asm)
     _compile(SYNC_LIB, defines=("H3_DEBUG_SYNC=1",), verbose=verbose)
+    _compile(TIMING_LIB, defines=("H3_PHASE_TIMING=1",), verbose=verbose)
     return LIB
 
 

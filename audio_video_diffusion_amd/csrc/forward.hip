@@ -53,6 +53,7 @@
 #include "common.h"
 #include "params.h"
 #include "rope_norm.h"
+#include "h3attn_phase_timing.h"
 
 namespace h3 {
 
@@ -246,6 +247,29 @@ __device__ __forceinline__ void debug_stage_sync() {
         __syncthreads();
     }
 }
+// Phase-timing build (compiled with -DH3_PHASE_TIMING=1 into a third
+// library, a measurement aid): every wave reads the shader clock (s_memtime)
+// at the start of each key tile, after its Q'K'^T chain, after its softmax,
+// after its last P V issue and after the tile's barrier, and at the ends of
+// its prologue, loop and epilogue; lane 0 adds the wave's sums into
+// g_phase_cycles (vector atomics) for its group of four waves (one wave per
+// SIMD: waves 4g..4g+3).  The stamps' results are consumed after the barrier,
+// so the waits they need fall there.  The release build compiles none of it.
+#ifndef H3_PHASE_TIMING
+#define H3_PHASE_TIMING 0
+#endif
+constexpr bool kPhaseTiming = H3_PHASE_TIMING != 0;
+// per wave group: Q'K'^T, softmax, P V issue, barrier, tiles, prologue, loop,
+// epilogue, waves (9 of kPhaseSlots)
+constexpr int kPhaseSlots = 10, kPhaseGroups = 3;
+#if H3_PHASE_TIMING
+__device__ unsigned long long g_phase_cycles[kPhaseSlots * kPhaseGroups];
+#endif
+__device__ __forceinline__ uint64_t phase_clock() {
+    if constexpr (kPhaseTiming) return __builtin_amdgcn_s_memtime();
+    return 0;
+}
+
 // Wait until at most kOutstanding of this wave's DMA instructions are still in
 // flight (vmcnt retires in issue order): with the newest fetches allowed
 // outstanding, every older tile has landed.
@@ -387,6 +411,9 @@ fwd8_kernel(FwdParams P) {
     const int n32 = lane & 31, hh = lane >> 5;
     const int q0 = qt * kBMw + wave * 32;
     const int n = P.n;
+    // phase timing (kPhaseTiming only): kernel start, tile-phase sums, loop bounds
+    [[maybe_unused]] const uint64_t ph_k0 = phase_clock();
+    [[maybe_unused]] uint64_t ph_sum[4] = {0, 0, 0, 0}, ph_l0 = 0, ph_l1 = 0, ph_tiles = 0;
 
     const uint8_t* qhead = static_cast<const uint8_t*>(P.q) + (int64_t)head * P.npad * D::kRowB;
     const uint8_t* khead = static_cast<const uint8_t*>(P.k) + (int64_t)head * P.npad * D::kRowB;
@@ -545,6 +572,8 @@ fwd8_kernel(FwdParams P) {
     // (j - 2 when staggered), which every wave has left at the last barrier.
     constexpr bool kLateFetch = kFp8V && !kInt8;
     auto tile = [&](int j, bool masked, int st) {
+        [[maybe_unused]] const uint64_t ph0 = phase_clock();
+        [[maybe_unused]] uint64_t ph1 = ph0, ph2 = ph0;
         if constexpr (!kLateFetch) fetch(j + kAhead);
         debug_stage_sync();
         // S^T of this wave's 32 queries: S[kb] = LDS rows 32kb..32kb+31
@@ -569,6 +598,7 @@ fwd8_kernel(FwdParams P) {
             // more than the 12 this compiler pads its own 32x32 products with on
             // gfx950 (s_nop 11 before a dependent VALU read)
             asm volatile("s_nop 7\n\ts_nop 4" : "+v"(Si[0]), "+v"(Si[1]));
+            ph1 = phase_clock();
             debug_stage_sync();
             // the fp32 values 1.5 * 2^23 + S (kI8Bias).  Whole-vector bit casts: a
             // bit cast of a single vector element is miscompiled by this compiler
@@ -596,6 +626,7 @@ fwd8_kernel(FwdParams P) {
             }
             if constexpr (kLateFetch) fetch(j + kAhead);
             asm volatile("s_nop 7\n\ts_nop 4" : "+v"(S[0]), "+v"(S[1]));      // as above
+            ph1 = phase_clock();
             debug_stage_sync();
         }
         if constexpr (kScores) {
@@ -694,6 +725,7 @@ fwd8_kernel(FwdParams P) {
                         t = (rs[0] + rs[1]) + (rs[2] + rs[3]);
                     }
                 l += t;
+                ph2 = phase_clock();
                 if (behind) tile_sync();
                 // O^T += V^T P'^T: lane (n32, hh) reads d-row 32cc + n32, keys 32hh..32hh+31
                 const uint8_t* vb_ = vbuf_st(st) + v_lane_off;
@@ -760,6 +792,7 @@ fwd8_kernel(FwdParams P) {
                         }
                     }
                 l += t;
+                ph2 = phase_clock();
                 if (behind) {
                     tile_sync();
                     __builtin_amdgcn_s_setprio(2);     // the lagging wave's P V (kStagger)
@@ -791,7 +824,16 @@ fwd8_kernel(FwdParams P) {
                 }
             }
         }
+        [[maybe_unused]] const uint64_t ph3 = phase_clock();
         if (!behind) tile_sync();
+        if constexpr (kPhaseTiming) {
+            const uint64_t ph4 = phase_clock();
+            ph_sum[0] += ph1 - ph0;
+            ph_sum[1] += ph2 - ph1;
+            ph_sum[2] += ph3 - ph2;
+            ph_sum[3] += ph4 - ph3;
+            ph_tiles += 1;
+        }
     };
 
     // the first tiles stream in while Q' is prepared (the int8 form prepares
@@ -948,6 +990,7 @@ fwd8_kernel(FwdParams P) {
     // (168 registers), so these keep the rolled loop.
     constexpr bool kUnroll = kFuseQ && kW == 8;
     int j = jb;
+    ph_l0 = phase_clock();
     if constexpr (kUnroll) {
         for (; j < last && (j & 3); ++j) tile(j, false, j & 3);
         for (; j + 4 <= last; j += 4) {
@@ -959,6 +1002,7 @@ fwd8_kernel(FwdParams P) {
     }
     for (; j < last; ++j) tile(j, false, j % kStages);
     tile(last, ragged, last % kStages);
+    ph_l1 = phase_clock();
     // the chain-start values stay allocated until every chain has read them
     if constexpr (kInt8) asm volatile("" ::"v"(bias16));
     if constexpr (kFuseBf) asm volatile("" ::"v"(negm));
@@ -988,6 +1032,16 @@ fwd8_kernel(FwdParams P) {
                 st8(orow + d0, w);
             }
     }
+#if H3_PHASE_TIMING
+    const uint64_t ph_k1 = phase_clock();
+    if (lane == 0) {
+        unsigned long long* g = g_phase_cycles + kPhaseSlots * (wave / 4);
+        const uint64_t v[9] = {ph_sum[0], ph_sum[1], ph_sum[2], ph_sum[3], ph_tiles,
+                               ph_l0 - ph_k0, ph_l1 - ph_l0, ph_k1 - ph_l1, 1};
+#pragma unroll
+        for (int i = 0; i < 9; ++i) atomicAdd(g + i, (unsigned long long)v[i]);
+    }
+#endif
 }
 
 hipError_t launch_forward(const FwdParams& P, bool int8, bool fp8v, hipStream_t stream) {
@@ -1031,3 +1085,23 @@ hipError_t launch_scores_i8(const FwdParams& P, bool fp8v_layout, hipStream_t st
 }
 
 }  // namespace h3
+
+// The phase-timing accessors (include/h3attn_phase_timing.h): live in the
+// phase-timing build, H3ATTN_E_UNSUPPORTED in the others.
+extern "C" int h3attn_phase_timing_read(unsigned long long* out) {
+#if H3_PHASE_TIMING
+    if (!out) return -1;
+    return hipMemcpyFromSymbol(out, HIP_SYMBOL(h3::g_phase_cycles), sizeof(h3::g_phase_cycles)) == hipSuccess ? 0 : -6;
+#else
+    (void)out;
+    return -3;
+#endif
+}
+extern "C" int h3attn_phase_timing_clear(void) {
+#if H3_PHASE_TIMING
+    static const unsigned long long zero[h3::kPhaseSlots * h3::kPhaseGroups] = {};
+    return hipMemcpyToSymbol(HIP_SYMBOL(h3::g_phase_cycles), zero, sizeof(zero)) == hipSuccess ? 0 : -6;
+#else
+    return -3;
+#endif
+}

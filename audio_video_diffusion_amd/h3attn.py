@@ -24,6 +24,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = globals().get("_LIB_PATH", os.path.join(PKG, "libh3attn.so"))
 # the race-detection build: a barrier after every LDS stage of the forward
 SYNC_LIB_PATH = os.path.join(PKG, "libh3attn_sync.so")
+# the phase-timing build: shader-clock stamps in the forward's tile loop
+TIMING_LIB_PATH = os.path.join(PKG, "libh3attn_timing.so")
+PHASE_TIMING_COUNTERS = 30
 
 QK_BF16 = 0
 QK_I8_BLK64 = 1
@@ -109,6 +112,8 @@ def _load():
         "h3attn_prep_k_i8": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, vp, vp, vp, vp]),
         "h3attn_forward_fused_q_i8": (ctypes.c_int, [pp, vp, i64, i64, vp, i64, vp, vp, vp, vp, i64, i64, vp, i64,
                                                      i64, f32, vp]),
+        "h3attn_phase_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_ulonglong)]),
+        "h3attn_phase_timing_clear": (ctypes.c_int, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -326,3 +331,19 @@ def calibrate_mfma_bf16(blocks: int, iters: int, out, stream=None):
     if rc:
         raise H3AttnError(rc, "h3attn_calibrate_mfma_bf16")
     return blocks * 8 * iters * 16 * 32768.0
+
+
+def phase_timing_clear():
+    """``h3attn_phase_timing_clear``: zero the counters (phase-timing build only)."""
+    rc = _lib.h3attn_phase_timing_clear()
+    if rc:
+        raise H3AttnError(rc, "h3attn_phase_timing_clear")
+
+
+def phase_timing_read():
+    """``h3attn_phase_timing_read``: the 30 counters as a list of ints (phase-timing build only)."""
+    buf = (ctypes.c_ulonglong * PHASE_TIMING_COUNTERS)()
+    rc = _lib.h3attn_phase_timing_read(buf)
+    if rc:
+        raise H3AttnError(rc, "h3attn_phase_timing_read")
+    return [int(x) for x in buf]

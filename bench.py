@@ -123,6 +123,9 @@ def parse():
                     help="only run a plain device copy of MIB MiB three times (counter calibration) and exit")
     ap.add_argument("--forms", action="store_true",
                     help="time each forward form on the workload (one JSON line per form) and exit")
+    ap.add_argument("--phase-timing", action="store_true",
+                    help="run each forward form from the phase-timing build (libh3attn_timing.so) and print "
+                         "where its tile loop spends its cycles (one JSON line per form), then exit")
     ap.add_argument("--full-oracle", action="store_true",
                     help="time the CPU oracle over whole workloads / 2,048-row subsets on a process pool and exit")
     ap.add_argument("--sweep-steps", type=int, default=20,
@@ -543,6 +546,50 @@ def forms(A, W, cfg, steps, warmup):
         torch.cuda.empty_cache()
 
 
+def phase_timing(A, W, cfg, steps, warmup):
+    """Every forward form on workload `cfg` from the phase-timing build: the
+    cycles per key tile of each wave group (waves 4g..4g+3, one per SIMD) from
+    the tile's start to the end of its Q'K'^T chain, through the softmax, to
+    the issue of its last P V product and to the end of its barrier, and the
+    cycles per wave of the prologue, the tile loop and the epilogue (sums over
+    the warmup and timed calls, divided by their counts).  One JSON line per form."""
+    import statistics
+    import torch
+    TA = A.variant(A.TIMING_LIB_PATH)
+    wl = W.WORKLOADS[cfg]
+    print(f"[bench] generating {wl.name}: N={wl.n_tokens} H={wl.heads}", file=sys.stderr, flush=True)
+    dev = W.device_inputs(W.make_inputs(cfg, wl, threads=16))
+    scale = 1.0 / math.sqrt(128.0)
+    for name, int8, fp8v, fused in FORMS:
+        print(f"[bench] phase timing {name}", file=sys.stderr, flush=True)
+        p = TA.problem(wl.n_tokens, wl.heads, TA.QK_I8_BLK64 if int8 else TA.QK_BF16)
+        q_out, k_out, qs, ks = TA.alloc_prepped(p)
+        vfp8 = TA.alloc_v_fp8(p) if fp8v else None
+        kmean = torch.empty((wl.heads, 128), dtype=torch.float32, device="cuda") if int8 and fp8v else None
+        o = torch.empty_like(dev["v"])
+        torch.cuda.synchronize()
+        TA.phase_timing_clear()
+        _, fwd_ms, _ = time_step(TA, p, dev, q_out, k_out, qs, ks, o, scale, steps, warmup, None, vfp8, kmean, fused)
+        torch.cuda.synchronize()
+        c = TA.phase_timing_read()
+        groups = []
+        for g in range(3):
+            v = c[10 * g:10 * g + 10]
+            tiles, waves = v[4], v[8]
+            if not waves:
+                continue
+            per = {k: round(v[i] / tiles, 1) for i, k in enumerate(("qk_chain", "softmax", "pv_issue", "to_barrier_end"))}
+            per["sum"] = round(sum(v[0:4]) / tiles, 1)
+            groups.append({"waves": f"{4 * g}-{4 * g + 3}", "wave_count": waves, "tiles_per_wave": round(tiles / waves, 2),
+                           "cycles_per_tile": per, "loop_cycles_per_tile": round(v[6] / tiles, 1),
+                           "prologue_cycles_per_wave": round(v[5] / waves), "epilogue_cycles_per_wave": round(v[7] / waves)})
+        print(json.dumps({"form": name, "workload": wl.name, "n_tokens": wl.n_tokens, "heads": wl.heads,
+                          "calls": steps + warmup, "forward_ms_median": round(statistics.median(fwd_ms), 4),
+                          "groups": groups}), flush=True)
+        del q_out, k_out, qs, ks, o, vfp8, kmean
+        torch.cuda.empty_cache()
+
+
 _ORACLE_HEAD = {}
 
 
@@ -647,6 +694,9 @@ def main():
     from audio_video_diffusion_amd import workloads as W
     if args.forms:
         forms(A, W, W.HEADLINE if args.config is None else args.config, args.steps, args.warmup)
+        return
+    if args.phase_timing:
+        phase_timing(A, W, W.HEADLINE if args.config is None else args.config, args.steps, args.warmup)
         return
 
     cfg = W.HEADLINE if args.config is None else args.config

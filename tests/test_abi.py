@@ -13,7 +13,9 @@ import pytest
 
 from audio_video_diffusion_amd import h3attn as A
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "h3attn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+HEADER = os.path.join(INCLUDE, "h3attn.h")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 F = 0x7f0000000000          # fake, 16-byte aligned "device" addresses, far apart
 G = 0x7f1000000000
@@ -24,14 +26,18 @@ K = 0x7f5000000000
 
 
 def declared_functions():
-    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
-    return sorted(set(re.findall(r"\b(h3attn_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(h3attn_\w+)\s*\(", text))
+    return sorted(names)
 
 
-@pytest.mark.parametrize("path", [A.LIB_PATH, A.SYNC_LIB_PATH], ids=["release", "race-detection"])
+@pytest.mark.parametrize("path", [A.LIB_PATH, A.SYNC_LIB_PATH, A.TIMING_LIB_PATH],
+                         ids=["release", "race-detection", "phase-timing"])
 def test_library_exports_every_declared_symbol(path):
     names = declared_functions()
-    assert {"h3attn_prep", "h3attn_forward", "h3attn_debug_scores_i32"} <= set(names)
+    assert {"h3attn_prep", "h3attn_forward", "h3attn_debug_scores_i32", "h3attn_phase_timing_read"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     exported = set(re.findall(r"\bT (h3attn_\w+)", out))
     lib = A.lib if path == A.LIB_PATH else A.variant(path).lib
@@ -335,3 +341,13 @@ def test_forward_fused_q_checks():
     assert fwd_fq(p, o=I + 64) == -5                         # output over the positions
     assert fwd_fq(p, o=G + 4096) == -5                       # output inside k'
     assert fwd_fq(p, o=K + 384 * 10) == -5                   # output inside v
+
+
+def test_phase_timing_calls_outside_the_timing_build():
+    # release and race-detection builds: unsupported, without touching the GPU
+    for lib in (A.lib, A.variant(A.SYNC_LIB_PATH).lib):
+        buf = (ctypes.c_ulonglong * A.PHASE_TIMING_COUNTERS)()
+        assert lib.h3attn_phase_timing_read(buf) == -3
+        assert lib.h3attn_phase_timing_clear() == -3
+    # the phase-timing build checks its pointer first
+    assert A.variant(A.TIMING_LIB_PATH).lib.h3attn_phase_timing_read(None) == -1
