@@ -62,11 +62,11 @@ PEAK_HBM_GBS = 8000.0
 FORWARD_TRAFFIC = {
     "workload": "1344x768_124f",
     "kernel": "h3attn_forward_fused_q",
-    "source_sha256": "72ccd9968a11aac64b0ed65e615f9063789097dd9da5bd6a6a21eabb1f0f8f64",
+    "source_sha256": "6aba5e5488bbc592f7d02772e849f9a9dcc39b6fdb7559ffa252928901c3a223",
     # the copy's kernel reads 524,319 KiB per 1 GiB as FETCH_SIZE (factor 2.0) and
     # writes 1,048,576 KiB as WRITE_SIZE (factor 1.0)
-    "fetch_kib": 13350855.3, "fetch_scale": 2.0,
-    "write_kib": 816515.6, "write_scale": 1.0,
+    "fetch_kib": 13350855.8, "fetch_scale": 2.0,
+    "write_kib": 817250.2, "write_scale": 1.0,
 }
 
 
