@@ -11,6 +11,11 @@ rows (all rows for small N) are compared with the oracle:
 * int8 forms: the oracle's attention on the int8 codes of the GPU's own bf16
   prep (the int8 stage, at the stage bounds), as in the fixed-size tests.
 
+A second list of cases runs the E4M3 P·V forward (bf16 or int8 Q'/K' from the
+prep, V staged by ``h3attn_prep_v_fp8``) against the oracle's exact softmax
+over the dequantised V with its P-rounding bound (``attention_fp8v_rows``), on
+the scores of the GPU's own prep output, as in ``test_gpu_fp8v.py``.
+
 The list of cases is drawn once from a fixed seed, so the test is
 deterministic; it spreads coverage over combinations the fixed tests leave
 out (odd tile tails with generic sections, per-head gamma with int8, ...).
@@ -24,6 +29,7 @@ from audio_video_diffusion_amd import h3attn as A
 from audio_video_diffusion_amd import workloads as W
 
 from gpu_util import MEAN_ABS, SCALE, check, f64, run_forward
+from test_gpu_fp8v import check_fp8, v_hat_of
 
 pytestmark = pytest.mark.gpu
 
@@ -116,3 +122,53 @@ def test_random_case_matches_oracle(case):
         ck, sk = O.quantize_i8(kv[hh, :n].astype(np.float32))
         ref.append(O.attention_i8_rows_head(rows, cq, sq, ck, sk, v[:, hh, :], SCALE))
     check(got, np.stack(ref, axis=1), max_abs=1e-2, mean_abs=MEAN_ABS, rel_l2=6e-3, what=f"case {i} {form} stage")
+
+
+def _draw_fp8_cases(n_cases=12, seed=0xF8F8):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n_cases):
+        n = int(round(np.exp(rng.uniform(0.0, np.log(5000.0))))) if rng.random() < 0.5 else int(rng.integers(600, 5001))
+        h = int(rng.integers(1, 4))
+        cut = np.sort(rng.choice(np.arange(0, 129, 2), size=2))
+        sections = (int(cut[0]), int(cut[1] - cut[0]), int(128 - cut[1]))
+        theta = float(rng.choice([10000.0, 500.0, 1e6]))
+        eps = float(rng.choice([1e-6, 1e-5, 0.0]))
+        cases.append((i, n, h, sections, theta, eps, bool(rng.random() < 0.5), bool(rng.random() < 0.5)))
+    return cases
+
+
+FP8_CASES = _draw_fp8_cases()
+
+
+@pytest.mark.parametrize("case", FP8_CASES,
+                         ids=[f"f{c[0]}-n{c[1]}-h{c[2]}-{'int8' if c[7] else 'bf16'}" for c in FP8_CASES])
+def test_random_case_fp8v_matches_oracle(case):
+    i, n, h, sections, theta, eps, per_head, int8 = case
+    print(f"    N={n} H={h} sections={sections} theta={theta} eps={eps} per_head={per_head} int8={int8}",
+          flush=True)
+    wl = W.ragged_workload(n, h)
+    inp = W.make_inputs(700 + i, wl, per_head_gamma=per_head)
+    dev = W.device_inputs(inp)
+    p = A.problem(n, h, A.QK_I8_BLK64 if int8 else A.QK_BF16, sections=sections, theta=theta, eps=eps)
+    q_out, k_out, qs, ks = A.alloc_prepped(p)
+    A.prep(p, dev["q"], dev["k"], dev["gamma_q"], dev["gamma_k"], dev["pos"], q_out, k_out, qs, ks)
+    codes, vsc = A.alloc_v_fp8(p)
+    A.prep_v_fp8(p, dev["v"], codes, vsc)
+    o = torch.empty_like(dev["v"])
+    A.forward_fp8v(p, q_out, k_out, codes, vsc, o, SCALE, qs, ks)
+    rows = _rows(n, 50 + i)
+    got = f64(o)[rows]
+    refs, bounds = [], []
+    for hh in range(h):
+        if int8:
+            cq, cs = q_out[hh, :n].cpu().numpy(), qs[hh].cpu().numpy().astype(np.float64)
+            ck, ksc = k_out[hh, :n].cpu().numpy(), ks[hh].cpu().numpy().astype(np.float64)
+            s = O.scores_i32(cq[rows], ck).astype(np.float64) * cs[rows // 64][:, None] \
+                * ksc[np.arange(n) // 64][None, :] * SCALE
+        else:
+            s = (f64(q_out)[hh, rows] @ f64(k_out)[hh, :n].T) * SCALE
+        ref, bound = O.attention_fp8v_rows(s, v_hat_of(inp.v[:, hh, :]))
+        refs.append(ref)
+        bounds.append(bound)
+    check_fp8(got.transpose(1, 0, 2), np.stack(refs), np.stack(bounds), what=f"case {i} fp8v int8={int8}")
