@@ -389,7 +389,8 @@ fwd8_kernel(FwdParams P) {
     // with E4M3 V -2.8% (the raised priority made it +5.5%), bf16 Q'/K' and V
     // -1.5 to -2.2% (+2.9% without the raised priority); the fused-Q form was
     // level with it (+0.4 to -0.5%) and keeps the common barrier, as do the
-    // twelve-wave int8 forms.
+    // twelve-wave int8 forms.  With the older group lagging instead (its P V
+    // then wins the arbitration unaided) every form was 4-8% slower.
     constexpr bool kStagger = kW == 8 && !kInt8 && !kScores && !kFuseQ;
     // tiles fetched ahead of the one being computed
     constexpr int kAhead = kStagger ? 2 : 3;
